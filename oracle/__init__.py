@@ -1,0 +1,182 @@
+"""CPU oracle for the MUSTAFAR hot path (ctypes binding of mustafar_oracle.cpp).
+
+TEST INFRASTRUCTURE ONLY: the plain fp64 / exact-integer definition that the
+HIP library is checked against.  Only tests/, the smoke check in
+__graft_entry__ and the CPU-baseline leg of bench.py may import this package.
+It shares no code with the HIP library (unstructured_sparse_kv_amd).
+
+Every function is pinned by CPU tests against things other than itself: see
+tests/test_oracle_*.py.  The pages print no worked example, so nothing here is
+pinned to a value printed on the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mustafar_oracle.cpp")
+_LIB = os.path.join(_HERE, "libmustafar_oracle.so")
+
+_lib = None
+
+P = ctypes.c_void_p
+I32, I64, F64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+
+
+def build(extra_flags: tuple = ()) -> str:
+    """Compile the oracle with the host C++ compiler (no HIP)."""
+    cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-pthread", *extra_flags, _SRC,
+           "-o", _LIB + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        L.orc_half_to_double.restype = F64
+        L.orc_half_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_half_to_double_array.argtypes = [P, I64, P]
+        L.orc_hardware_threads.restype = ctypes.c_int
+        L.orc_keep_from_sparsity.restype = ctypes.c_int
+        L.orc_keep_from_sparsity.argtypes = [F64, ctypes.c_int]
+        L.orc_prune_rows.argtypes = [P, I64, ctypes.c_int, ctypes.c_int, P]
+        L.orc_compress.restype = ctypes.c_int
+        L.orc_compress.argtypes = [P, ctypes.c_int, ctypes.c_int, I64, ctypes.c_int, P, ctypes.c_int,
+                                   I64, P, P, P, ctypes.c_int]
+        L.orc_decompress.restype = ctypes.c_int
+        L.orc_decompress.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, I64, ctypes.c_int,
+                                     ctypes.c_int, P, P]
+        L.orc_used_bytes.restype = I64
+        L.orc_used_bytes.argtypes = [ctypes.c_int, ctypes.c_int, P, I64, ctypes.c_int, ctypes.c_int]
+        L.orc_attention_dense.restype = ctypes.c_int
+        L.orc_attention_dense.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          P, P, I64, P, F64, P, ctypes.c_int]
+        L.orc_attention_compressed.restype = ctypes.c_int
+        L.orc_attention_compressed.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, P, P, P, ctypes.c_int, P, P, P,
+                                               ctypes.c_int, I64, P, F64, P, I64, P, ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    """fp16 data (numpy float16/uint16 or a CPU torch tensor) as contiguous uint16 bits."""
+    if hasattr(a, "detach"):
+        import torch
+        a = a.detach().cpu().contiguous().view(torch.int16).numpy()
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint16)
+
+
+def hardware_threads() -> int:
+    return lib().orc_hardware_threads()
+
+
+def half_to_double(bits: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    lib().orc_half_to_double_array(_p(b), b.size, _p(out))
+    return out
+
+
+def keep_from_sparsity(s: float, d: int = 128) -> int:
+    return lib().orc_keep_from_sparsity(float(s), int(d))
+
+
+def prune_rows(x, k: int) -> np.ndarray:
+    """x: [..., d] fp16 -> uint8 keep mask of the same shape."""
+    x = _u16(x)
+    d = x.shape[-1]
+    keep = np.zeros(x.shape, dtype=np.uint8)
+    lib().orc_prune_rows(_p(x), x.size // d, d, int(k), _p(keep))
+    return keep
+
+
+class Compressed:
+    """One compressed tensor: bitmaps [B][H][cap][d/64] u64, values [B][H][cap*k] u16,
+    tile_off [B][H][cap/64+1] u32."""
+
+    def __init__(self, B, H, cap, d, k):
+        self.B, self.H, self.cap, self.d, self.k = B, H, cap, d, k
+        self.bitmaps = np.zeros((B, H, cap, d // 64), dtype=np.uint64)
+        self.values = np.zeros((B, H, cap * k), dtype=np.uint16)
+        self.tile_off = np.zeros((B, H, cap // 64 + 1), dtype=np.uint32)
+
+
+def compress(dense, seq_lens, k: int, cap: int | None = None, nthreads: int = 0) -> Compressed:
+    """dense: [B][H][T][d] fp16 -> Compressed (rows >= seq_lens[b] left zero)."""
+    x = _u16(dense)
+    B, H, T, d = x.shape
+    cap = T if cap is None else cap
+    cap = (cap + 63) // 64 * 64
+    seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    c = Compressed(B, H, cap, d, k)
+    rc = lib().orc_compress(_p(x), B, H, T, d, _p(seq), int(k), cap, _p(c.bitmaps), _p(c.values),
+                            _p(c.tile_off), int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_compress: bad arguments")
+    return c
+
+
+def decompress(c: Compressed, seq_lens) -> np.ndarray:
+    seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    out = np.empty((c.B, c.H, c.cap, c.d), dtype=np.uint16)
+    rc = lib().orc_decompress(_p(c.bitmaps), _p(c.values), _p(c.tile_off), c.B, c.H, c.cap, c.d,
+                              c.k, _p(seq), _p(out))
+    if rc != 0:
+        raise ValueError("orc_decompress: bad arguments")
+    return out
+
+
+def used_bytes(B, H, seq_lens, cap, d, k) -> int:
+    seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    return int(lib().orc_used_bytes(B, H, _p(seq), cap, d, k))
+
+
+def attention_dense(q, K, V, seq_lens, scale: float, nthreads: int = 0) -> np.ndarray:
+    """q [B][Hq][d], K/V [B][Hkv][T][d] fp16 -> out [B][Hq][d] float64."""
+    qb, Kb, Vb = _u16(q), _u16(K), _u16(V)
+    B, Hq, d = qb.shape
+    Hkv, T = Kb.shape[1], Kb.shape[2]
+    seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    rc = lib().orc_attention_dense(_p(qb), B, Hq, Hkv, d, _p(Kb), _p(Vb), T, _p(seq), float(scale),
+                                   _p(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_attention_dense: bad arguments")
+    return out
+
+
+def attention_compressed(q, kc: Compressed, vc: Compressed, seq_lens, scale: float,
+                         units=None, nthreads: int = 0) -> np.ndarray:
+    """Attention over compressed caches; `units` = list of b*Hq+hq to compute (others stay 0)."""
+    qb = _u16(q)
+    B, Hq, d = qb.shape
+    seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    if units is None:
+        up, n = None, 0
+    else:
+        u = np.ascontiguousarray(np.asarray(units, dtype=np.int64))
+        up, n = _p(u), u.size
+    rc = lib().orc_attention_compressed(_p(qb), B, Hq, kc.H, d, _p(kc.bitmaps), _p(kc.values),
+                                        _p(kc.tile_off), kc.k, _p(vc.bitmaps), _p(vc.values),
+                                        _p(vc.tile_off), vc.k, kc.cap, _p(seq), float(scale), up, n,
+                                        _p(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_attention_compressed: bad arguments")
+    return out

@@ -1,0 +1,324 @@
+// MUSTAFAR hot path: CPU oracle.
+//
+// TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously-correct
+// definition that the HIP library is checked against.  Only the tests, the
+// smoke check and the benchmark's CPU-baseline leg may load it; the product
+// path never does.  It shares no code, header, table or helper with the HIP
+// library: its fp16 decoder, its top-k rule, its encoder and its attention are
+// written here from their definitions, in fp64 for floating point and exact
+// integers for everything else.
+//
+// Sources (web pages; cited by title and section):
+//   [Summary]  "MUSTAFAR: Promoting Unstructured Sparsity for KV Cache Pruning
+//              in LLM Inference", AI-written paper summary (research map page),
+//              sections "Approach", "Key results", "Limitations".
+//   [README]   "Mustafar: Promoting Unstructured Sparsity for KV Cache Pruning
+//              in LLM Inference", repository README mirror, sections
+//              "Part II: LongBench Evaluation", "Part III: Kernel Evaluation".
+//   [Abstract] "Mustafar: Promoting Unstructured Sparsity for KV Cache Pruning
+//              in LLM Inference", author abstract (author page).
+//
+// Readings where the pages are silent (each one also listed in the design doc):
+//   R1 pruning unit: one (batch, kv-head, token) row of head_dim channels.
+//   R2 survivors k = floor((1 - s) * d + 0.5), clamped to [0, d].
+//   R3 magnitude: |x| of the fp16 value, compared through bits & 0x7FFF.
+//   R4 ties: the lower channel index survives.
+//   R5 the bitmap marks the k selected channels (so popcount == k).
+//   R6 layout: two 64-bit words per 128-channel row, bit j of word w is
+//      channel 64w + j; kept values in ascending channel order; one u32
+//      offset per 64-row tile (plus an end entry).
+//   R7 a pruned entry decompresses to +0.0.
+//   R8 attention scale is passed in (1/sqrt(d) in the tests).
+//   R9 q head hq reads kv head floor(hq / (Hq / Hkv)).
+//   R14 an empty sequence gives an all-zero output.
+//
+// Parity status: every function here is pinned by the CPU tests (fp16
+// decoder: exhaustive against IEEE-754 binary16; prune: brute force over all
+// k-subsets and hand-worked fixtures; encode/decode: round trip and closed-form
+// sizes; attention: torch's scaled_dot_product_attention in fp64, closed forms
+// T=1 and q=0, GQA == MHA with repeated heads).  The pages print no worked
+// example, so nothing here is pinned to a value printed on the pages.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <numeric>
+#include <thread>
+#include <vector>
+
+namespace {
+
+// IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+double half_to_double(uint16_t h) {
+  const int sign = h >> 15;
+  const int e = (h >> 10) & 0x1F;
+  const int m = h & 0x3FF;
+  double v;
+  if (e == 0) {
+    v = std::ldexp(static_cast<double>(m), -24);  // subnormal: m * 2^-24
+  } else if (e == 31) {
+    v = m ? std::nan("") : INFINITY;
+  } else {
+    v = std::ldexp(static_cast<double>(1024 + m), e - 25);  // (1 + m/2^10) * 2^(e-15)
+  }
+  return sign ? -v : v;
+}
+
+// R3: magnitude key of an fp16 value.  For finite values the ordering of
+// (bits & 0x7FFF) as an unsigned integer is the ordering of |x|, and -0 == +0.
+inline uint16_t mag_key(uint16_t h) { return static_cast<uint16_t>(h & 0x7FFF); }
+
+// Per-token magnitude pruning of one row ([Summary] "Approach"; [Abstract];
+// the token-wise, magnitude-based variant named in [README] "Part II"):
+// keep the k channels of largest magnitude, ties to the lower channel (R4).
+// Written as: stable sort of the channel indices by key, descending; the
+// first k are the survivors.
+void prune_row(const uint16_t* x, int d, int k, uint8_t* keep) {
+  std::vector<int> idx(d);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(),
+                   [&](int a, int b) { return mag_key(x[a]) > mag_key(x[b]); });
+  std::memset(keep, 0, d);
+  for (int i = 0; i < k && i < d; ++i) keep[idx[i]] = 1;
+}
+
+int clamp_len(int32_t t, int64_t cap) {
+  if (t < 0) return 0;
+  return static_cast<int>(std::min<int64_t>(t, cap));
+}
+
+template <class F>
+void parallel_for(int64_t n, int nthreads, F&& f) {
+  if (nthreads <= 1 || n <= 1) {
+    for (int64_t i = 0; i < n; ++i) f(i);
+    return;
+  }
+  nthreads = static_cast<int>(std::min<int64_t>(nthreads, n));
+  std::vector<std::thread> th;
+  for (int w = 0; w < nthreads; ++w) {
+    th.emplace_back([&, w] {
+      for (int64_t i = w; i < n; i += nthreads) f(i);
+    });
+  }
+  for (auto& t : th) t.join();
+}
+
+int hw_threads() {
+  unsigned n = std::thread::hardware_concurrency();
+  return n ? static_cast<int>(n) : 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+double orc_half_to_double(uint16_t h) { return half_to_double(h); }
+
+void orc_half_to_double_array(const uint16_t* h, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = half_to_double(h[i]);
+}
+
+int orc_hardware_threads(void) { return hw_threads(); }
+
+// R2: survivors per row for a pruned fraction s ([README] "Part II": the
+// target sparsity is the fraction pruned, 0.5 or 0.7).  -1 for s outside [0,1].
+int orc_keep_from_sparsity(double s, int d) {
+  if (!(s >= 0.0 && s <= 1.0) || d <= 0) return -1;
+  const double x = (1.0 - s) * static_cast<double>(d);
+  int k = static_cast<int>(std::floor(x + 0.5));
+  if (k < 0) k = 0;
+  if (k > d) k = d;
+  return k;
+}
+
+// Prune n rows of d channels; keep[r*d + c] = 1 for survivors.
+void orc_prune_rows(const uint16_t* x, int64_t n, int d, int k, uint8_t* keep) {
+  for (int64_t r = 0; r < n; ++r) prune_row(x + r * d, d, k, keep + r * d);
+}
+
+// Compress a dense cache [B][H][t_stride][d] (fp16 bits) into the bitmap format
+// ([Summary] "Approach": a bitmap-based compressed format; [Abstract]):
+//   bitmaps  [B][H][cap][d/64] u64   bit j of word w <=> channel 64w+j kept (R5, R6)
+//   values   [B][H][cap*k]     fp16  kept values, ascending channel, rows in order
+//   tile_off [B][H][cap/64+1]  u32   tile_off[j] = number of kept values in rows
+//                                    r < min(64 j, T_b) of that (b, h)
+// Rows r >= T_b = min(seq_lens[b], cap, t_stride) are not written; nor are
+// tile_off entries j > ceil(T_b / 64).  Returns 0, or -1 on bad arguments.
+int orc_compress(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
+                 const int32_t* seq_lens, int k, int64_t cap, uint64_t* bitmaps,
+                 uint16_t* values, uint32_t* tile_off, int nthreads) {
+  if (d <= 0 || d % 64 != 0 || k < 0 || k > d || cap <= 0 || cap % 64 != 0) return -1;
+  const int words = d / 64;
+  const int64_t ntile_entries = cap / 64 + 1;
+  if (nthreads <= 0) nthreads = hw_threads();
+  parallel_for(static_cast<int64_t>(B) * H, nthreads, [&](int64_t u) {
+    const int64_t b = u / H;
+    const int T = clamp_len(seq_lens[b], std::min<int64_t>(cap, t_stride));
+    const uint16_t* src = dense + u * t_stride * d;
+    uint64_t* bm = bitmaps + u * cap * words;
+    uint16_t* val = values + u * cap * k;
+    uint32_t* toff = tile_off + u * ntile_entries;
+    std::vector<uint8_t> keep(d);
+    uint32_t count = 0;
+    for (int r = 0; r < T; ++r) {
+      if (r % 64 == 0) toff[r / 64] = count;
+      const uint16_t* x = src + static_cast<int64_t>(r) * d;
+      prune_row(x, d, k, keep.data());
+      for (int w = 0; w < words; ++w) bm[static_cast<int64_t>(r) * words + w] = 0;
+      for (int c = 0; c < d; ++c) {
+        if (keep[c]) {
+          bm[static_cast<int64_t>(r) * words + c / 64] |= (uint64_t{1} << (c % 64));
+          val[count++] = x[c];
+        }
+      }
+    }
+    toff[(T + 63) / 64] = count;
+  });
+  return 0;
+}
+
+// Decompress (R7): walk the bitmap; a set bit takes the next stored value, a
+// clear bit gives +0.0.  Output [B][H][cap][d] fp16 bits; rows >= T_b are zero.
+int orc_decompress(const uint64_t* bitmaps, const uint16_t* values, const uint32_t* tile_off,
+                   int B, int H, int64_t cap, int d, int k, const int32_t* seq_lens,
+                   uint16_t* out) {
+  if (d <= 0 || d % 64 != 0 || cap <= 0 || cap % 64 != 0) return -1;
+  const int words = d / 64;
+  const int64_t ntile_entries = cap / 64 + 1;
+  for (int64_t u = 0; u < static_cast<int64_t>(B) * H; ++u) {
+    const int64_t b = u / H;
+    const int T = clamp_len(seq_lens[b], cap);
+    const uint64_t* bm = bitmaps + u * cap * words;
+    const uint16_t* val = values + u * cap * k;
+    const uint32_t* toff = tile_off + u * ntile_entries;
+    uint16_t* dst = out + u * cap * d;
+    std::memset(dst, 0, sizeof(uint16_t) * cap * d);
+    for (int tile = 0; tile * 64 < T; ++tile) {
+      uint32_t next = toff[tile];  // first value of the tile
+      for (int r = tile * 64; r < std::min(T, tile * 64 + 64); ++r) {
+        for (int c = 0; c < d; ++c) {
+          const bool set = (bm[static_cast<int64_t>(r) * words + c / 64] >> (c % 64)) & 1u;
+          dst[static_cast<int64_t>(r) * d + c] = set ? val[next++] : 0;
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+// Bytes a compressed tensor occupies for the given lengths: per (b, h),
+// bitmaps (d/8 bytes per row) + kept values (2 bytes each) + tile offsets
+// (4 bytes per tile entry, ceil(T/64) + 1 entries).
+int64_t orc_used_bytes(int B, int H, const int32_t* seq_lens, int64_t cap, int d, int k) {
+  int64_t total = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t T = clamp_len(seq_lens[b], cap);
+    total += static_cast<int64_t>(H) * (T * (d / 8) + 2 * T * k + 4 * ((T + 63) / 64 + 1));
+  }
+  return total;
+}
+
+// Decode-step attention, the plain definition, fp64 ([Summary] "Approach":
+// attention computed over the pruned caches; [Abstract]):
+//   s_t = scale * sum_c q[c] * K[t][c]
+//   o[c] = sum_t exp(s_t - max s) V[t][c] / sum_t exp(s_t - max s)
+// for each (b, hq) with kv head h = floor(hq / (Hq / Hkv)) (R9).  K, V are
+// dense fp16 caches [B][Hkv][t_stride][d] (pass the zero-masked cache to get
+// the sparse result).  T_b = min(seq_lens[b], t_stride); T_b = 0 gives zeros.
+// out: [B][Hq][d] double.
+int orc_attention_dense(const uint16_t* q, int B, int Hq, int Hkv, int d, const uint16_t* K,
+                        const uint16_t* V, int64_t t_stride, const int32_t* seq_lens,
+                        double scale, double* out, int nthreads) {
+  if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0) return -1;
+  const int G = Hq / Hkv;
+  if (nthreads <= 0) nthreads = hw_threads();
+  parallel_for(static_cast<int64_t>(B) * Hq, nthreads, [&](int64_t u) {
+    const int64_t b = u / Hq, hq = u % Hq, h = hq / G;
+    const int T = clamp_len(seq_lens[b], t_stride);
+    double* o = out + u * d;
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    if (T == 0) return;
+    const uint16_t* qv = q + u * d;
+    const uint16_t* Kb = K + (b * Hkv + h) * t_stride * d;
+    const uint16_t* Vb = V + (b * Hkv + h) * t_stride * d;
+    std::vector<double> qd(d), s(T);
+    for (int c = 0; c < d; ++c) qd[c] = half_to_double(qv[c]);
+    for (int t = 0; t < T; ++t) {
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c) acc += qd[c] * half_to_double(Kb[static_cast<int64_t>(t) * d + c]);
+      s[t] = scale * acc;
+    }
+    const double m = *std::max_element(s.begin(), s.end());
+    double l = 0.0;
+    for (int t = 0; t < T; ++t) {
+      const double w = std::exp(s[t] - m);
+      l += w;
+      for (int c = 0; c < d; ++c) o[c] += w * half_to_double(Vb[static_cast<int64_t>(t) * d + c]);
+    }
+    for (int c = 0; c < d; ++c) o[c] /= l;
+  });
+  return 0;
+}
+
+// The same attention read directly from the compressed caches: each row is
+// decompressed by the rule of orc_decompress (R7) into fp64, then the plain
+// definition above is applied.  Only the (b, hq) pairs listed in `units`
+// (n_units entries of b*Hq + hq; all pairs when units == nullptr) are computed
+// and written to out[b][hq][:].  kk and kv are the survivor counts of K and V.
+int orc_attention_compressed(const uint16_t* q, int B, int Hq, int Hkv, int d,
+                             const uint64_t* kbm, const uint16_t* kval, const uint32_t* ktoff,
+                             int kk, const uint64_t* vbm, const uint16_t* vval,
+                             const uint32_t* vtoff, int kvk, int64_t cap,
+                             const int32_t* seq_lens, double scale, const int64_t* units,
+                             int64_t n_units, double* out, int nthreads) {
+  if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d % 64 != 0 || cap % 64 != 0) return -1;
+  const int G = Hq / Hkv;
+  const int words = d / 64;
+  const int64_t ntile_entries = cap / 64 + 1;
+  if (nthreads <= 0) nthreads = hw_threads();
+  const int64_t n = units ? n_units : static_cast<int64_t>(B) * Hq;
+  auto decode_rows = [&](const uint64_t* bm, const uint16_t* val, const uint32_t* toff, int k,
+                         int64_t unit, int T, std::vector<double>& dst) {
+    const uint64_t* ub = bm + unit * cap * words;
+    const uint16_t* uv = val + unit * cap * k;
+    const uint32_t* ut = toff + unit * ntile_entries;
+    dst.assign(static_cast<size_t>(T) * d, 0.0);
+    for (int tile = 0; tile * 64 < T; ++tile) {
+      uint32_t next = ut[tile];
+      for (int r = tile * 64; r < std::min(T, tile * 64 + 64); ++r)
+        for (int c = 0; c < d; ++c)
+          if ((ub[static_cast<int64_t>(r) * words + c / 64] >> (c % 64)) & 1u)
+            dst[static_cast<size_t>(r) * d + c] = half_to_double(uv[next++]);
+    }
+  };
+  parallel_for(n, nthreads, [&](int64_t i) {
+    const int64_t u = units ? units[i] : i;
+    const int64_t b = u / Hq, hq = u % Hq, h = hq / G;
+    const int64_t unit = b * Hkv + h;
+    const int T = clamp_len(seq_lens[b], cap);
+    double* o = out + u * d;
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    if (T == 0) return;
+    std::vector<double> Kd, Vd, qd(d), s(T);
+    decode_rows(kbm, kval, ktoff, kk, unit, T, Kd);
+    decode_rows(vbm, vval, vtoff, kvk, unit, T, Vd);
+    for (int c = 0; c < d; ++c) qd[c] = half_to_double(q[u * d + c]);
+    for (int t = 0; t < T; ++t) {
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c) acc += qd[c] * Kd[static_cast<size_t>(t) * d + c];
+      s[t] = scale * acc;
+    }
+    const double m = *std::max_element(s.begin(), s.end());
+    double l = 0.0;
+    for (int t = 0; t < T; ++t) {
+      const double w = std::exp(s[t] - m);
+      l += w;
+      for (int c = 0; c < d; ++c) o[c] += w * Vd[static_cast<size_t>(t) * d + c];
+    }
+    for (int c = 0; c < d; ++c) o[c] /= l;
+  });
+  return 0;
+}
+
+}  // extern "C"
