@@ -1,0 +1,232 @@
+/*
+ * mustafar.h -- C ABI of the MUSTAFAR hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The library prunes the key and value caches of decode-time attention per
+ * token by magnitude to an arbitrary unstructured sparsity, stores them in a
+ * bitmap-compressed format, and computes the decode-step attention (q.K^T,
+ * softmax, P.V) directly over the compressed caches.  A dense fp16 decode
+ * attention is exported beside it as the comparison baseline.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [Summary]  "MUSTAFAR: Promoting Unstructured Sparsity for KV Cache Pruning in
+ *              LLM Inference", AI-written paper summary (research-map page),
+ *              sections "Approach", "Key results", "Limitations".
+ *   [README]   "Mustafar: Promoting Unstructured Sparsity for KV Cache Pruning in
+ *              LLM Inference", repository README mirror, sections
+ *              "Part II: LongBench Evaluation", "Part III: Kernel Evaluation".
+ *   [Abstract] "Mustafar: Promoting Unstructured Sparsity for KV Cache Pruning in
+ *              LLM Inference", author abstract (author page).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked (device) are HIP device memory; (host) is host memory.
+ *     The caller allocates and owns every buffer; the library never allocates,
+ *     frees or synchronises.
+ *   - fp16 data travels as its IEEE-754 binary16 bit patterns (uint16_t).
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Work is enqueued on it and the call returns without waiting.
+ *   - Every call checks its arguments on the host first and returns a negative
+ *     mustafar_status without launching anything when one is bad; only then
+ *     does it look for a device (MUSTAFAR_ENODEV when there is none) and
+ *     launch.  A launch failure returns MUSTAFAR_ELAUNCH.
+ *   - head_dim must be 128.  Device pointers must be 16-byte aligned.
+ *   - Lengths in seq_lens (device) are read by the kernels and clamped to
+ *     [0, capacity]; the host cannot see them.
+ *   - No global mutable state: calls on different streams and buffers may run
+ *     concurrently from any thread.
+ */
+#ifndef MUSTAFAR_H_
+#define MUSTAFAR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MUSTAFAR_OK = 0,
+  MUSTAFAR_EINVAL = -1,       /* bad argument: null / misaligned pointer, size out of range */
+  MUSTAFAR_EUNSUPPORTED = -2, /* valid but not built: head_dim != 128, Hq/Hkv not in {1,2,4,8} */
+  MUSTAFAR_ENODEV = -3,       /* no HIP device visible */
+  MUSTAFAR_ELAUNCH = -4,      /* kernel launch failed (hipGetLastError after the launch) */
+  MUSTAFAR_ENOSPACE = -5      /* workspace smaller than the call needs */
+} mustafar_status;
+
+/* Sticky device status bits written by mustafar_append_token. */
+#define MUSTAFAR_STATUS_APPEND_FULL 1u /* a sequence was already at capacity; its row was dropped */
+
+/*
+ * One compressed tensor (the key cache or the value cache of one layer) in the
+ * bitmap-based sparse format ([Summary] "Approach"; [Abstract]).  The exact
+ * layout is this library's design:
+ *
+ *   bitmaps      (device) uint64 [batch][num_kv_heads][capacity][2]
+ *                bit j of word w is set <=> channel 64*w + j of that row was kept.
+ *   values       (device) uint16 [batch][num_kv_heads][capacity * keep]
+ *                the kept fp16 values of each row in ascending channel order,
+ *                rows of a (batch, head) stored back to back from row 0.
+ *   tile_offsets (device) uint32 [batch][num_kv_heads][capacity / 64 + 1]
+ *                entry j = number of kept values stored before row 64*j of that
+ *                (batch, head), for j = 0 .. ceil(T/64) (the last one is the end
+ *                of the stored values); under per-token pruning entry j equals
+ *                min(64*j, T) * keep.
+ *
+ * capacity is the number of rows allocated per (batch, head): a positive
+ * multiple of 64.  keep (0..head_dim) is the number of survivors per row.
+ */
+typedef struct {
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t keep;
+  int32_t capacity;
+  uint64_t *bitmaps;
+  uint16_t *values;
+  uint32_t *tile_offsets;
+} mustafar_kv_t;
+
+/* Text for a status code (static storage; never NULL). */
+const char *mustafar_status_str(int status);
+
+/*
+ * Survivors per row for a target sparsity s = fraction of entries pruned
+ * ([README] "Part II": k_sparsity / v_sparsity, 0.5 means 50% pruned).
+ * Returns floor((1 - s) * head_dim + 0.5) clamped to [0, head_dim]
+ * (64 at s = 0.5, 38 at s = 0.7), or MUSTAFAR_EINVAL when s is not in [0, 1]
+ * or head_dim <= 0.  Host only.
+ */
+int mustafar_keep_from_sparsity(double sparsity, int32_t head_dim);
+
+/*
+ * Bytes to allocate for each array of a compressed tensor described by `kv`
+ * (its pointers are ignored).  values_bytes includes 64 bytes of tail padding.
+ * Host only.  Returns MUSTAFAR_OK or MUSTAFAR_EINVAL/EUNSUPPORTED.
+ */
+int mustafar_kv_alloc_bytes(const mustafar_kv_t *kv, uint64_t *bitmaps_bytes,
+                            uint64_t *values_bytes, uint64_t *offsets_bytes);
+
+/*
+ * Bytes the compressed tensor occupies for the given lengths (host array of
+ * `batch` entries, clamped to [0, capacity]): per (batch, head) with T rows,
+ * 16*T (bitmaps) + 2*keep*T (values) + 4*(ceil(T/64) + 1) (tile offsets).
+ * This is the compressed size compared with the dense 256*T bytes
+ * ([Summary] "Key results" gives 45% of dense at 70% sparsity and 65% at 50%
+ * for the authors' own layout).  Host only.
+ */
+int mustafar_kv_used_bytes(const mustafar_kv_t *kv, const int32_t *seq_lens_host, int64_t *bytes);
+
+/*
+ * Prefill: prune every cached row of a dense cache per token by magnitude and
+ * write it compressed into `dst` ([Summary] "Approach"; [Abstract]; the
+ * token-wise, magnitude-based variant Kt_Mag / Vt_Mag of [README] "Part II").
+ *
+ *   dense     (device) uint16 [batch][num_kv_heads][t_stride][128] fp16 bits.
+ *   seq_lens  (device) int32 [batch]; rows t < min(seq_lens[b], capacity, t_stride)
+ *             are compressed, the rest of dst is left untouched except the
+ *             tile-offset end entry.
+ *
+ * Row rule: the keep channels of largest |x| survive, compared through the
+ * magnitude bits (bits & 0x7FFF, so -0 == +0); on equal magnitude the lower
+ * channel survives.  Bitmaps, values and tile offsets are bit-exact
+ * functions of the input.
+ */
+int mustafar_prune_compress(const mustafar_kv_t *dst, const uint16_t *dense, int64_t t_stride,
+                            const int32_t *seq_lens, void *stream);
+
+/*
+ * Decode-time append: prune and compress the new key and value row of every
+ * (batch, kv head) by the same rule and store them as row T_b = seq_lens[b] of
+ * `k` and `v`, then increment seq_lens[b] once ([Summary] "Approach" and
+ * [Abstract]: the tokens produced during decode are pruned and compressed at
+ * run time).  k and v must agree in batch, num_kv_heads and capacity and may
+ * differ in keep.
+ *
+ *   k_new, v_new (device) uint16 [batch][num_kv_heads][128] fp16 bits.
+ *   seq_lens     (device) int32 [batch], incremented in place.
+ *   status       (device) uint32, may be NULL; MUSTAFAR_STATUS_APPEND_FULL is
+ *                OR-ed in when a sequence is already at capacity (that
+ *                sequence is then left unchanged).
+ */
+int mustafar_append_token(const mustafar_kv_t *k, const mustafar_kv_t *v, const uint16_t *k_new,
+                          const uint16_t *v_new, int32_t *seq_lens, uint32_t *status,
+                          void *stream);
+
+/*
+ * Splits over the sequence that mustafar_decode_attn / mustafar_dense_decode_attn
+ * use when called with splits = 0, for this shape.  Host only.
+ */
+int mustafar_decode_auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);
+
+/*
+ * Workspace bytes the decode calls need for `splits` splits (0 = automatic,
+ * sized from max_seq_len).  Host only.
+ */
+int mustafar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_seq_len, int32_t splits,
+                                    uint64_t *bytes);
+
+/*
+ * Prepare a workspace (device, `bytes` long) for the decode calls: clears the
+ * per-(batch, kv head) completion counters.  Call once after allocating it;
+ * each decode call leaves the counters cleared again.  Calls that share a
+ * workspace must be ordered (same stream); overlapping ones race.
+ */
+int mustafar_decode_workspace_init(void *workspace, uint64_t bytes, void *stream);
+
+/*
+ * Decode-step attention over the compressed caches ([Summary] "Approach": an
+ * attention kernel that computes directly on the bitmap format; [Abstract];
+ * [README] "Part III": the batched sparse attention kernel).  For every batch
+ * row b and query head hq, with kv head h = floor(hq / (num_q_heads / num_kv_heads))
+ * and T_b = min(seq_lens[b], capacity):
+ *     s_t = scale * sum_c q[b][hq][c] * Khat[b][h][t][c]
+ *     out[b][hq][c] = sum_t exp(s_t - max s) Vhat[b][h][t][c] / sum_t exp(s_t - max s)
+ * where Khat/Vhat are the stored rows with pruned entries 0; T_b = 0 gives 0.
+ *
+ *   q    (device) uint16 [batch][num_q_heads][128] fp16 bits.
+ *   k, v compressed caches with equal batch, num_kv_heads and capacity.
+ *   seq_lens (device) int32 [batch].
+ *   max_seq_len  host upper bound of seq_lens, used only to pick splits.
+ *   scale        softmax scale (1/sqrt(128) for standard attention).
+ *   splits       number of sequence splits per (batch, kv head); 0 = automatic.
+ *   out  (device) uint16 [batch][num_q_heads][128] fp16 bits (round to nearest).
+ *   workspace    (device) from mustafar_decode_workspace_bytes, initialised once
+ *                with mustafar_decode_workspace_init.
+ * Arithmetic: fp16 inputs, fp32 products and accumulation, fp32 online softmax
+ * per split and a cross-split merge.  One kernel launch.
+ */
+int mustafar_decode_attn(const uint16_t *q, int32_t num_q_heads, const mustafar_kv_t *k,
+                         const mustafar_kv_t *v, const int32_t *seq_lens, int32_t max_seq_len,
+                         float scale, int32_t splits, uint16_t *out, void *workspace,
+                         uint64_t workspace_bytes, void *stream);
+
+/*
+ * The same attention over dense, unpruned fp16 caches: the comparison
+ * baseline (the pages compare against dense attention, [Summary] "Key results"
+ * and "Experimental setup").  q.K^T runs on the matrix cores (MFMA), P.V and
+ * the softmax on the vector units.
+ *
+ *   k, v (device) uint16 [batch][num_kv_heads][t_stride][128] fp16 bits; rows
+ *        t < min(seq_lens[b], t_stride) are attended.
+ *   Other arguments as mustafar_decode_attn (the workspace rules are the same).
+ */
+int mustafar_dense_decode_attn(const uint16_t *q, int32_t num_q_heads, const uint16_t *k,
+                               const uint16_t *v, int32_t batch, int32_t num_kv_heads,
+                               int32_t head_dim, int64_t t_stride, const int32_t *seq_lens,
+                               int32_t max_seq_len, float scale, int32_t splits, uint16_t *out,
+                               void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
+ * Measurement helper: read `bytes` (a multiple of 4096, >= 4096) from `buf`
+ * (device, 16-byte aligned) with coalesced 16-byte loads and write a checksum
+ * to *sink (device uint32) so the reads cannot be elided.  Used to measure
+ * the achievable HBM read rate on the same device.
+ */
+int mustafar_probe_stream_read(const void *buf, uint64_t bytes, uint32_t *sink, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUSTAFAR_H_ */

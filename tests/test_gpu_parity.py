@@ -1,0 +1,295 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same
+fp16 bits.  Compressed caches must match bit for bit; attention within max-abs
+1e-2 and relative L2 1e-3 of the fp64 oracle."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import unstructured_sparse_kv_amd as usk
+from tests.gpu_helpers import (SCALE, assert_attn_close, assert_compressed_equal, compress_on_gpu,
+                               oracle_attention_units, say, u16)
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _decode(q, kc, vc, seq_dev, max_len, splits=0):
+    B, Hq = q.shape[0], q.shape[1]
+    ws = usk.make_workspace(B, Hq, kc.num_kv_heads, max_len, splits)
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device=q.device)
+    usk.decode_attn(q, kc, vc, seq_dev, max_len, SCALE, out, ws, splits)
+    torch.cuda.synchronize()
+    return out
+
+
+def _dense(q, K, V, seq_dev, max_len, splits=0):
+    B, Hq = q.shape[0], q.shape[1]
+    ws = usk.make_workspace(B, Hq, K.shape[1], max_len, splits)
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device=q.device)
+    usk.dense_decode_attn(q, K, V, seq_dev, max_len, SCALE, out, ws, splits)
+    torch.cuda.synchronize()
+    return out
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def test_tiny_end_to_end(gpu):
+    cfg = synth.CONFIGS["tiny"]
+    K, V, q, seq = synth.make_inputs(cfg)
+    keep = usk.keep_from_sparsity(cfg.sparsity)
+    say(f"tiny: keep={keep} T={cfg.T}")
+    seq_d = seq.to(gpu)
+    kc = compress_on_gpu(K.to(gpu), seq_d, keep, cfg.T)
+    vc = compress_on_gpu(V.to(gpu), seq_d, keep, cfg.T)
+    torch.cuda.synchronize()
+    ko, vo = oracle.compress(K, seq, keep, cfg.T), oracle.compress(V, seq, keep, cfg.T)
+    assert_compressed_equal(kc, ko, seq)
+    assert_compressed_equal(vc, vo, seq)
+    out = _decode(q.to(gpu), kc, vc, seq_d, cfg.T)
+    assert_attn_close(_f64(out), oracle.attention_compressed(q, ko, vo, seq, SCALE), "tiny sparse")
+    outd = _dense(q.to(gpu), K.to(gpu), V.to(gpu), seq_d, cfg.T)
+    assert_attn_close(_f64(outd), oracle.attention_dense(q, K, V, seq, SCALE), "tiny dense")
+
+
+def _row_from_case(case):
+    row = np.full(128, np.float16(case["default"]), dtype=np.float16).view(np.uint16)
+    for ch, v in case["set"].items():
+        if isinstance(v, str) and v.startswith("0x"):
+            row[int(ch)] = int(v, 16)
+        elif v == "-0":
+            row[int(ch)] = 0x8000
+        else:
+            row[int(ch)] = np.float16(v).view(np.uint16)
+    return row
+
+
+def test_crafted_rows_bitexact(gpu):
+    cases = json.load(open(os.path.join(GOLDEN, "prune_worked_examples.json")))["cases"]
+    for case in cases:
+        row = _row_from_case(case)
+        x = torch.from_numpy(row.view(np.int16).reshape(1, 1, 1, 128).copy())
+        say(f"crafted case {case['name']} keep={case['k']}")
+        c = compress_on_gpu(x.to(gpu), torch.ones(1, dtype=torch.int32, device=gpu), case["k"], 64)
+        bm, vals, _ = c.views()
+        assert [f"{int(w) & (2**64 - 1):016x}" for w in bm[0, 0, 0].cpu()] == case["bitmap_hex"], case["name"]
+        assert [f"{int(v) & 0xFFFF:04x}" for v in vals[0, 0, :case["k"]].cpu()] == case["values_hex"]
+    # tie-heavy rows: coarse integer values, +-0, subnormals, every keep
+    rng = np.random.default_rng(99)
+    rows = np.concatenate([
+        (rng.integers(-3, 4, (96, 128)).astype(np.float16)).view(np.uint16),
+        rng.choice(np.array([0, 0x8000, 1, 0x8001, 0x7BFF, 0xFBFF, 0x3C00], np.uint16), (32, 128)),
+        rng.standard_normal((64, 128)).astype(np.float16).view(np.uint16),
+    ])
+    x = torch.from_numpy(rows.view(np.int16).reshape(1, 1, -1, 128).copy())
+    seq = np.array([rows.shape[0]], np.int32)
+    for keep in (0, 1, 2, 37, 38, 63, 64, 65, 100, 127, 128):
+        say(f"tie rows keep={keep}")
+        c = compress_on_gpu(x.to(gpu), torch.from_numpy(seq).to(gpu), keep, 192)
+        torch.cuda.synchronize()
+        assert_compressed_equal(c, oracle.compress(x, seq, keep, 192), seq)
+
+
+def _small_inputs(B, Hq, Hkv, T, seed):
+    g = torch.Generator().manual_seed(seed)
+    K = torch.randn(B, Hkv, T, 128, generator=g, dtype=torch.float64)
+    K[..., [3, 77]] *= 8
+    V = torch.randn(B, Hkv, T, 128, generator=g, dtype=torch.float64)
+    q = torch.randn(B, Hq, 128, generator=g, dtype=torch.float64)
+    return K.half(), V.half(), q.half()
+
+
+@pytest.mark.parametrize("kk,kv", [(0, 0), (1, 1), (3, 3), (13, 13), (37, 37), (38, 38), (47, 49),
+                                   (64, 64), (65, 65), (101, 101), (127, 127), (128, 128), (38, 100),
+                                   (100, 2)])
+def test_keep_sweep(gpu, kk, kv):
+    B, Hq, Hkv, T = 3, 8, 2, 200
+    K, V, q = _small_inputs(B, Hq, Hkv, T, kk * 131 + kv)
+    seq = np.array([200, 77, 1], np.int32)
+    say(f"keep sweep kk={kk} kv={kv}")
+    seq_d = torch.from_numpy(seq).to(gpu)
+    kc = compress_on_gpu(K.to(gpu), seq_d, kk, 256)
+    vc = compress_on_gpu(V.to(gpu), seq_d, kv, 256)
+    torch.cuda.synchronize()
+    ko, vo = oracle.compress(K, seq, kk, 256), oracle.compress(V, seq, kv, 256)
+    assert_compressed_equal(kc, ko, seq)
+    assert_compressed_equal(vc, vo, seq)
+    ref = oracle.attention_compressed(q, ko, vo, seq, SCALE)
+    for splits in (0, 1, 3):
+        out = _decode(q.to(gpu), kc, vc, seq_d, 200, splits)
+        assert_attn_close(_f64(out), ref, f"kk={kk} kv={kv} splits={splits}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_group_sizes(gpu, G):
+    B, Hkv, T = 2, 2, 333
+    Hq = G * Hkv
+    K, V, q = _small_inputs(B, Hq, Hkv, T, 1000 + G)
+    seq = np.array([333, 130], np.int32)
+    say(f"group size G={G}")
+    seq_d = torch.from_numpy(seq).to(gpu)
+    kc = compress_on_gpu(K.to(gpu), seq_d, 38, 384)
+    vc = compress_on_gpu(V.to(gpu), seq_d, 38, 384)
+    out = _decode(q.to(gpu), kc, vc, seq_d, 333)
+    ko, vo = oracle.compress(K, seq, 38, 384), oracle.compress(V, seq, 38, 384)
+    assert_attn_close(_f64(out), oracle.attention_compressed(q, ko, vo, seq, SCALE), f"sparse G={G}")
+    outd = _dense(q.to(gpu), K.to(gpu), V.to(gpu), seq_d, 333)
+    assert_attn_close(_f64(outd), oracle.attention_dense(q, K, V, seq, SCALE), f"dense G={G}")
+
+
+def test_llama2_layer_full(gpu):
+    cfg = synth.CONFIGS["llama2_7b_layer"]
+    K, V, q, seq = synth.make_inputs(cfg)
+    keep = usk.keep_from_sparsity(cfg.sparsity)
+    say(f"llama2 layer: B=1 H=32 T=4096 keep={keep}")
+    seq_d = seq.to(gpu)
+    kc = compress_on_gpu(K.to(gpu), seq_d, keep, cfg.T)
+    vc = compress_on_gpu(V.to(gpu), seq_d, keep, cfg.T)
+    torch.cuda.synchronize()
+    ko, vo = oracle.compress(K, seq, keep, cfg.T), oracle.compress(V, seq, keep, cfg.T)
+    assert_compressed_equal(kc, ko, seq)
+    assert_compressed_equal(vc, vo, seq)
+    assert kc.used_bytes(seq.numpy()) + vc.used_bytes(seq.numpy()) == \
+        2 * oracle.used_bytes(1, 32, seq.numpy(), cfg.T, 128, keep)
+    out = _decode(q.to(gpu), kc, vc, seq_d, cfg.T)
+    assert_attn_close(_f64(out), oracle.attention_compressed(q, ko, vo, seq, SCALE), "llama2 sparse")
+    outd = _dense(q.to(gpu), K.to(gpu), V.to(gpu), seq_d, cfg.T)
+    assert_attn_close(_f64(outd), oracle.attention_dense(q, K, V, seq, SCALE), "llama2 dense")
+
+
+def test_llama3_layer_sampled(gpu):
+    cfg = synth.CONFIGS["llama3_8b_layer"]
+    say("llama3 layer: generating B=8 Hkv=8 T=32768 on the GPU")
+    K, V, q, seq = synth.make_inputs(cfg, device=gpu)
+    keep = usk.keep_from_sparsity(cfg.sparsity)
+    seq_d = seq.to(gpu)
+    kc = compress_on_gpu(K, seq_d, keep, cfg.T)
+    vc = compress_on_gpu(V, seq_d, keep, cfg.T)
+    torch.cuda.synchronize()
+    units = [(0, 0), (3, 5), (7, 7)]
+    Kc = torch.stack([K[b, h] for b, h in units])[:, None].cpu()
+    Vc = torch.stack([V[b, h] for b, h in units])[:, None].cpu()
+    seq_u = np.array([cfg.T] * len(units), np.int32)
+    ko, vo = oracle.compress(Kc, seq_u, keep, cfg.T), oracle.compress(Vc, seq_u, keep, cfg.T)
+    say("llama3 layer: bit-exact check of sampled units")
+    assert_compressed_equal(kc, ko, seq.numpy(), units, [(i, 0) for i in range(len(units))])
+    assert_compressed_equal(vc, vo, seq.numpy(), units, [(i, 0) for i in range(len(units))])
+    pairs = [(0, 0), (0, 3), (3, 21), (7, 31)]
+    Kcpu, Vcpu, qcpu = K.cpu(), V.cpu(), q.cpu()
+    ref = oracle_attention_units(qcpu, Kcpu, Vcpu, seq.numpy(), keep, keep, cfg.T, pairs, 4)
+    refd = {}
+    for b, hq in pairs:
+        h = hq // 4
+        refd[(b, hq)] = oracle.attention_dense(qcpu[b:b + 1, hq:hq + 1], Kcpu[b:b + 1, h:h + 1],
+                                               Vcpu[b:b + 1, h:h + 1], [cfg.T], SCALE)[0, 0]
+    outs = {}
+    for splits in (0, 1, 7, 64):
+        say(f"llama3 layer: sparse decode splits={splits}")
+        out = _decode(q, kc, vc, seq_d, cfg.T, splits)
+        outs[splits] = out.clone()
+        got = np.stack([_f64(out[b, hq]) for b, hq in pairs])
+        assert_attn_close(got, np.stack([ref[p] for p in pairs]), f"llama3 sparse splits={splits}")
+    again = _decode(q, kc, vc, seq_d, cfg.T, 0)
+    assert torch.equal(again, outs[0]), "decode is not deterministic"
+    say("llama3 layer: dense baseline")
+    outd = _dense(q, K, V, seq_d, cfg.T)
+    got = np.stack([_f64(outd[b, hq]) for b, hq in pairs])
+    assert_attn_close(got, np.stack([refd[p] for p in pairs]), "llama3 dense")
+
+
+def test_ragged_append_sequence(gpu):
+    cfg = synth.CONFIGS["mistral_ragged_append"]
+    keep = usk.keep_from_sparsity(cfg.sparsity)
+    seq0 = synth.seq_lens_uniform(cfg.seed, cfg.B, *cfg.ragged)
+    Tmax = cfg.ragged[1]
+    cap = Tmax + 64
+    say(f"ragged append: B=16 Hkv=8 lens {seq0.min().item()}..{seq0.max().item()} keep={keep} "
+        f"steps={cfg.steps}")
+    K, V, _, _ = synth.make_inputs(cfg, device=gpu, T=cap)
+    seq_d = seq0.to(gpu)
+    kc = compress_on_gpu(K, seq_d, keep, cap)
+    vc = compress_on_gpu(V, seq_d, keep, cap)
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    ws = usk.make_workspace(cfg.B, cfg.Hq, cfg.Hkv, cap)
+    out = torch.empty((cfg.B, cfg.Hq, 128), dtype=torch.float16, device=gpu)
+    pairs = [(0, 0), (5, 13), (9, 30), (15, 7)]
+    check_steps = {1, 2, 32, cfg.steps}
+    for step in range(1, cfg.steps + 1):
+        kn, vn, q = synth.step_inputs(cfg, step - 1, device=gpu)
+        usk.append_token(kc, vc, kn, vn, seq_d, status)
+        usk.decode_attn(q, kc, vc, seq_d, cap, SCALE, out, ws)
+        # the oracle sees the same new rows written into its dense copy
+        T_old = seq0 + (step - 1)
+        for b in range(cfg.B):
+            K[b, :, T_old[b]] = kn[b]
+            V[b, :, T_old[b]] = vn[b]
+        if step in check_steps:
+            torch.cuda.synchronize()
+            seq_now = (seq0 + step).numpy()
+            assert np.array_equal(seq_d.cpu().numpy(), seq_now)
+            say(f"ragged append: step {step} parity")
+            qcpu = q.cpu()
+            got, exp = [], []
+            for b, hq in pairs:
+                h = hq // 4
+                T = int(seq_now[b])
+                s1 = np.array([T], np.int32)
+                ko = oracle.compress(K[b:b + 1, h:h + 1, :T].cpu(), s1, keep, cap)
+                vo = oracle.compress(V[b:b + 1, h:h + 1, :T].cpu(), s1, keep, cap)
+                exp.append(oracle.attention_compressed(qcpu[b:b + 1, hq:hq + 1], ko, vo, s1, SCALE)[0, 0])
+                got.append(_f64(out[b, hq]))
+                if step == cfg.steps:
+                    assert_compressed_equal(kc, ko, seq_now, [(b, h)], [(0, 0)])
+                    assert_compressed_equal(vc, vo, seq_now, [(b, h)], [(0, 0)])
+            assert_attn_close(np.stack(got), np.stack(exp), f"ragged append step {step}")
+    assert status.item() == 0
+
+
+def test_edge_cases(gpu):
+    B, Hq, Hkv, T = 4, 4, 2, 130
+    K, V, q = _small_inputs(B, Hq, Hkv, T, 7)
+    seq = np.array([0, 1, 130, 500], np.int32)  # empty, one row, full, beyond capacity (clamped to 192)
+    cap = 192
+    Kp = torch.zeros(B, Hkv, cap, 128, dtype=torch.float16)
+    Vp = torch.zeros(B, Hkv, cap, 128, dtype=torch.float16)
+    Kp[:, :, :T], Vp[:, :, :T] = K, V
+    Kp[3], Vp[3] = torch.randn(Hkv, cap, 128).half(), torch.randn(Hkv, cap, 128).half()
+    say("edge cases: lengths 0, 1, 130, 500 (capacity 192)")
+    seq_d = torch.from_numpy(seq).to(gpu)
+    kc = compress_on_gpu(Kp.to(gpu), seq_d, 38, cap)
+    vc = compress_on_gpu(Vp.to(gpu), seq_d, 38, cap)
+    torch.cuda.synchronize()
+    seq_c = np.minimum(seq, cap)
+    ko, vo = oracle.compress(Kp, seq_c, 38, cap), oracle.compress(Vp, seq_c, 38, cap)
+    assert_compressed_equal(kc, ko, seq_c)
+    assert_compressed_equal(vc, vo, seq_c)
+    # canaries around the output
+    ws = usk.make_workspace(B, Hq, Hkv, cap)
+    buf = torch.full((B * Hq * 128 + 2 * 256,), 0x7E01, dtype=torch.int16, device=gpu)  # NaN pattern
+    out = buf[256:256 + B * Hq * 128].view(torch.float16).view(B, Hq, 128)
+    usk.decode_attn(q.to(gpu), kc, vc, seq_d, cap, SCALE, out, ws)
+    torch.cuda.synchronize()
+    assert (buf[:256] == 0x7E01).all() and (buf[-256:] == 0x7E01).all(), "canary overwritten"
+    ref = oracle.attention_compressed(q, ko, vo, seq_c, SCALE)
+    assert not out[0].any(), "empty sequence must give zeros"
+    assert_attn_close(_f64(out), ref, "edge cases")
+    # T = 1: the output is the stored first value row for every head of the group
+    v0 = oracle.decompress(vo, seq_c)[1, :, 0].view(np.float16).astype(np.float64)
+    for hq in range(Hq):
+        assert np.array_equal(_f64(out[1, hq]), v0[hq // 2].astype(np.float16).astype(np.float64))
+    # append at capacity: status bit, caches and lengths unchanged
+    full = torch.tensor([cap, cap, cap, cap], dtype=torch.int32, device=gpu)
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    before = [t.clone() for t in kc.views()]
+    usk.append_token(kc, vc, K[:, :, 0].contiguous().to(gpu), V[:, :, 0].contiguous().to(gpu), full, status)
+    torch.cuda.synchronize()
+    assert status.item() == usk.STATUS_APPEND_FULL
+    assert full.cpu().tolist() == [cap] * 4
+    for a, b in zip(before, kc.views()):
+        assert torch.equal(a, b)

@@ -1,0 +1,262 @@
+// C ABI of the MUSTAFAR library: host-side argument checks, launch geometry,
+// workspace sizing and byte accounting.  Every check runs before any HIP call,
+// so argument errors are reported without a device.
+#include <math.h>
+#include <string.h>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+using namespace mustafar;
+
+namespace {
+
+constexpr int kMaxSplits = 1024;
+constexpr int64_t kMaxCapacity = 1 << 24;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int check_kv_shape(const mustafar_kv_t* kv) {
+  if (!kv) return MUSTAFAR_EINVAL;
+  if (kv->batch <= 0 || kv->num_kv_heads <= 0) return MUSTAFAR_EINVAL;
+  if (kv->head_dim <= 0) return MUSTAFAR_EINVAL;
+  if (kv->head_dim != kHeadDim) return MUSTAFAR_EUNSUPPORTED;
+  if (kv->keep < 0 || kv->keep > kv->head_dim) return MUSTAFAR_EINVAL;
+  if (kv->capacity <= 0 || kv->capacity % 64 != 0 || kv->capacity > kMaxCapacity)
+    return MUSTAFAR_EINVAL;
+  // per-(batch, head) value region must be addressable with 32-bit byte offsets
+  if ((int64_t)kv->capacity * kv->keep * 2 >= (int64_t)1 << 31) return MUSTAFAR_EINVAL;
+  return MUSTAFAR_OK;
+}
+
+int check_kv(const mustafar_kv_t* kv) {
+  int rc = check_kv_shape(kv);
+  if (rc) return rc;
+  if (!kv->bitmaps || !kv->values || !kv->tile_offsets) return MUSTAFAR_EINVAL;
+  if (!aligned16(kv->bitmaps) || !aligned16(kv->values) || !aligned4(kv->tile_offsets))
+    return MUSTAFAR_EINVAL;
+  return MUSTAFAR_OK;
+}
+
+int check_device() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return MUSTAFAR_ENODEV;
+  }
+  return MUSTAFAR_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? MUSTAFAR_OK : MUSTAFAR_ELAUNCH; }
+
+int auto_splits(int64_t batch, int64_t hkv, int64_t max_seq_len) {
+  const int64_t units = batch * hkv;
+  const int64_t tiles = (max_seq_len + 63) / 64;
+  const int64_t target_blocks = 1024;  // about four 4-wave blocks per compute unit
+  int64_t s = (target_blocks + units - 1) / units;
+  const int64_t most = (tiles + 2 * kDecodeWaves - 1) / (2 * kDecodeWaves);  // >= 2 tiles per wave
+  if (s > most) s = most;
+  if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return (int)s;
+}
+
+int decode_common_checks(const uint16_t* q, int32_t hq, int32_t batch, int32_t hkv, int32_t max_seq_len,
+                         float scale, int32_t splits, const uint16_t* out, const void* ws,
+                         uint64_t ws_bytes, const int32_t* seq_lens, int* splits_out) {
+  if (!q || !out || !ws || !seq_lens) return MUSTAFAR_EINVAL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws) || !aligned4(seq_lens))
+    return MUSTAFAR_EINVAL;
+  if (hq <= 0 || hkv <= 0 || batch <= 0) return MUSTAFAR_EINVAL;
+  if (hq % hkv != 0) return MUSTAFAR_EINVAL;
+  const int g = hq / hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return MUSTAFAR_EUNSUPPORTED;
+  if (max_seq_len < 0 || splits < 0 || splits > kMaxSplits) return MUSTAFAR_EINVAL;
+  if (!isfinite(scale)) return MUSTAFAR_EINVAL;
+  if (batch > 65535 || hkv > 65535) return MUSTAFAR_EINVAL;  // grid z and y
+  const int sp = splits ? splits : auto_splits(batch, hkv, max_seq_len);
+  const uint64_t need = workspace_counter_bytes(batch, hkv) + workspace_partial_bytes(batch, hq, sp);
+  if (ws_bytes < need) return MUSTAFAR_ENOSPACE;
+  *splits_out = sp;
+  return MUSTAFAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mustafar_status_str(int status) {
+  switch (status) {
+    case MUSTAFAR_OK: return "ok";
+    case MUSTAFAR_EINVAL: return "invalid argument";
+    case MUSTAFAR_EUNSUPPORTED: return "unsupported configuration";
+    case MUSTAFAR_ENODEV: return "no HIP device";
+    case MUSTAFAR_ELAUNCH: return "kernel launch failed";
+    case MUSTAFAR_ENOSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int mustafar_keep_from_sparsity(double sparsity, int32_t head_dim) {
+  if (!(sparsity >= 0.0 && sparsity <= 1.0) || head_dim <= 0) return MUSTAFAR_EINVAL;
+  int k = (int)floor((1.0 - sparsity) * (double)head_dim + 0.5);
+  if (k < 0) k = 0;
+  if (k > head_dim) k = head_dim;
+  return k;
+}
+
+int mustafar_kv_alloc_bytes(const mustafar_kv_t* kv, uint64_t* bitmaps_bytes,
+                            uint64_t* values_bytes, uint64_t* offsets_bytes) {
+  const int rc = check_kv_shape(kv);
+  if (rc) return rc;
+  if (!bitmaps_bytes || !values_bytes || !offsets_bytes) return MUSTAFAR_EINVAL;
+  const uint64_t units = (uint64_t)kv->batch * kv->num_kv_heads;
+  *bitmaps_bytes = units * kv->capacity * (kv->head_dim / 64) * 8;
+  *values_bytes = units * kv->capacity * kv->keep * 2 + 64;
+  *offsets_bytes = units * (kv->capacity / 64 + 1) * 4;
+  return MUSTAFAR_OK;
+}
+
+int mustafar_kv_used_bytes(const mustafar_kv_t* kv, const int32_t* seq_lens_host, int64_t* bytes) {
+  const int rc = check_kv_shape(kv);
+  if (rc) return rc;
+  if (!seq_lens_host || !bytes) return MUSTAFAR_EINVAL;
+  int64_t total = 0;
+  for (int b = 0; b < kv->batch; ++b) {
+    int64_t T = seq_lens_host[b];
+    T = T < 0 ? 0 : (T > kv->capacity ? kv->capacity : T);
+    total += (int64_t)kv->num_kv_heads *
+             (T * (kv->head_dim / 8) + 2 * T * kv->keep + 4 * ((T + 63) / 64 + 1));
+  }
+  *bytes = total;
+  return MUSTAFAR_OK;
+}
+
+int mustafar_prune_compress(const mustafar_kv_t* dst, const uint16_t* dense, int64_t t_stride,
+                            const int32_t* seq_lens, void* stream) {
+  int rc = check_kv(dst);
+  if (rc) return rc;
+  if (!dense || !seq_lens || !aligned16(dense) || !aligned4(seq_lens)) return MUSTAFAR_EINVAL;
+  if (t_stride <= 0 || t_stride > kMaxCapacity * 64) return MUSTAFAR_EINVAL;
+  if ((rc = check_device())) return rc;
+  return launched(launch_prune_compress(*dst, dense, t_stride, seq_lens, (hipStream_t)stream));
+}
+
+int mustafar_append_token(const mustafar_kv_t* k, const mustafar_kv_t* v, const uint16_t* k_new,
+                          const uint16_t* v_new, int32_t* seq_lens, uint32_t* status,
+                          void* stream) {
+  int rc = check_kv(k);
+  if (rc) return rc;
+  if ((rc = check_kv(v))) return rc;
+  if (k->batch != v->batch || k->num_kv_heads != v->num_kv_heads || k->capacity != v->capacity)
+    return MUSTAFAR_EINVAL;
+  if (!k_new || !v_new || !seq_lens) return MUSTAFAR_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned4(seq_lens)) return MUSTAFAR_EINVAL;
+  if (status && !aligned4(status)) return MUSTAFAR_EINVAL;
+  if (k->batch > 65535) return MUSTAFAR_EINVAL;
+  if ((rc = check_device())) return rc;
+  return launched(launch_append(*k, *v, k_new, v_new, seq_lens, status, (hipStream_t)stream));
+}
+
+int mustafar_decode_auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
+  if (batch <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return MUSTAFAR_EINVAL;
+  return auto_splits(batch, num_kv_heads, max_seq_len);
+}
+
+int mustafar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_seq_len, int32_t splits,
+                                    uint64_t* bytes) {
+  if (!bytes || batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
+      splits < 0 || splits > kMaxSplits)
+    return MUSTAFAR_EINVAL;
+  if (head_dim != kHeadDim) return MUSTAFAR_EUNSUPPORTED;
+  if (num_q_heads % num_kv_heads != 0) return MUSTAFAR_EINVAL;
+  const int sp = splits ? splits : auto_splits(batch, num_kv_heads, max_seq_len);
+  *bytes = workspace_counter_bytes(batch, num_kv_heads) +
+           workspace_partial_bytes(batch, num_q_heads, sp);
+  return MUSTAFAR_OK;
+}
+
+int mustafar_decode_workspace_init(void* workspace, uint64_t bytes, void* stream) {
+  if (!workspace || !aligned16(workspace) || bytes == 0 || bytes % 4 != 0) return MUSTAFAR_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(launch_zero_u32((uint32_t*)workspace, bytes / 4, (hipStream_t)stream));
+}
+
+int mustafar_decode_attn(const uint16_t* q, int32_t num_q_heads, const mustafar_kv_t* k,
+                         const mustafar_kv_t* v, const int32_t* seq_lens, int32_t max_seq_len,
+                         float scale, int32_t splits, uint16_t* out, void* workspace,
+                         uint64_t workspace_bytes, void* stream) {
+  int rc = check_kv(k);
+  if (rc) return rc;
+  if ((rc = check_kv(v))) return rc;
+  if (k->batch != v->batch || k->num_kv_heads != v->num_kv_heads || k->capacity != v->capacity)
+    return MUSTAFAR_EINVAL;
+  int sp = 0;
+  rc = decode_common_checks(q, num_q_heads, k->batch, k->num_kv_heads, max_seq_len, scale, splits,
+                            out, workspace, workspace_bytes, seq_lens, &sp);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
+  SparseDecodeArgs a;
+  a.q = q;
+  a.Hq = num_q_heads;
+  a.Hkv = k->num_kv_heads;
+  a.cap = k->capacity;
+  a.kk = k->keep;
+  a.vk = v->keep;
+  a.splits = sp;
+  a.kbm = k->bitmaps;
+  a.kval = k->values;
+  a.ktoff = k->tile_offsets;
+  a.vbm = v->bitmaps;
+  a.vval = v->values;
+  a.vtoff = v->tile_offsets;
+  a.seq_lens = seq_lens;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  a.out = out;
+  a.counters = (uint32_t*)workspace;
+  a.part = (float*)((char*)workspace + workspace_counter_bytes(k->batch, k->num_kv_heads));
+  return launched(launch_decode_sparse(a, k->batch, (hipStream_t)stream));
+}
+
+int mustafar_dense_decode_attn(const uint16_t* q, int32_t num_q_heads, const uint16_t* k,
+                               const uint16_t* v, int32_t batch, int32_t num_kv_heads,
+                               int32_t head_dim, int64_t t_stride, const int32_t* seq_lens,
+                               int32_t max_seq_len, float scale, int32_t splits, uint16_t* out,
+                               void* workspace, uint64_t workspace_bytes, void* stream) {
+  if (!k || !v || !aligned16(k) || !aligned16(v)) return MUSTAFAR_EINVAL;
+  if (head_dim <= 0) return MUSTAFAR_EINVAL;
+  if (head_dim != kHeadDim) return MUSTAFAR_EUNSUPPORTED;
+  if (t_stride <= 0 || t_stride * kHeadDim * 2 >= ((int64_t)1 << 32)) return MUSTAFAR_EINVAL;
+  int sp = 0;
+  int rc = decode_common_checks(q, num_q_heads, batch, num_kv_heads, max_seq_len, scale, splits,
+                                out, workspace, workspace_bytes, seq_lens, &sp);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
+  DenseDecodeArgs a;
+  a.q = q;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.splits = sp;
+  a.t_stride = t_stride;
+  a.k = k;
+  a.v = v;
+  a.seq_lens = seq_lens;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.out = out;
+  a.counters = (uint32_t*)workspace;
+  a.part = (float*)((char*)workspace + workspace_counter_bytes(batch, num_kv_heads));
+  return launched(launch_decode_dense(a, batch, (hipStream_t)stream));
+}
+
+int mustafar_probe_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || !aligned16(buf) || !aligned4(sink)) return MUSTAFAR_EINVAL;
+  if (bytes < 4096 || bytes % 4096 != 0) return MUSTAFAR_EINVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(launch_stream_read(buf, bytes, sink, (hipStream_t)stream));
+}
+
+}  // extern "C"

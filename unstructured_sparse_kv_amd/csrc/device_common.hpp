@@ -1,0 +1,96 @@
+// Device helpers shared by the MUSTAFAR kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mustafar {
+
+constexpr int kHeadDim = 128;
+constexpr int kWave = 64;
+constexpr int kTile = 64;  // rows per tile: one row per lane
+
+// Raw buffer resource word 3 for the gfx9 family (untyped 32-bit dwords).
+constexpr int kBufferWord3 = 0x00020000;
+
+typedef __attribute__((address_space(4))) const uint64_t* ConstU64;
+typedef __attribute__((address_space(4))) const uint32_t* ConstU32;
+
+__device__ __forceinline__ uint32_t lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Bounds-checked buffer view: loads past `bytes` return 0 instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+}
+
+// Number of set bits of `mask` below this lane, plus `add`.
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t mask, uint32_t add) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, add));
+}
+
+// v if this lane's bit of the (wave-uniform) lane mask is set, else 0: one v_cndmask
+// with the mask in an SGPR pair.
+__device__ __forceinline__ uint32_t keep_if_lane_bit(uint64_t lane_mask, uint32_t v) {
+  uint32_t r;
+  asm("v_cndmask_b32 %0, 0, %1, %2" : "=v"(r) : "v"(v), "s"(lane_mask));
+  return r;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+__device__ __forceinline__ uint16_t float_to_half_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
+}
+
+// Lanes of one wave exchanging data through LDS: the hardware performs one
+// wave's LDS operations in issue order, so only the compiler must be kept from
+// moving or forwarding memory accesses across the exchange point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  asm volatile("" ::: "memory");
+}
+
+template <class T>
+__device__ __forceinline__ T wave_uniform(T x) {
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, kWave));
+  return x;
+}
+// Exclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t x) {
+  const uint32_t lane = lane_id();
+  uint32_t incl = x;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t y = (uint32_t)__shfl_up((int)incl, o, kWave);
+    if (lane >= (uint32_t)o) incl += y;
+  }
+  return incl - x;
+}
+
+}  // namespace mustafar

@@ -1,0 +1,62 @@
+// Internal launchers of the MUSTAFAR kernels (called by the C ABI in api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mustafar.h"
+
+namespace mustafar {
+
+constexpr int kDecodeWaves = 4;        // waves per decode block
+constexpr int kDecodeBlock = kDecodeWaves * 64;
+constexpr int kPartStride = 132;       // floats per (unit, split, q head) partial: m, l, acc[128], pad
+
+struct SparseDecodeArgs {
+  const uint16_t* q;
+  int32_t Hq, Hkv, cap, kk, vk, splits;
+  const uint64_t* kbm;
+  const uint16_t* kval;
+  const uint32_t* ktoff;
+  const uint64_t* vbm;
+  const uint16_t* vval;
+  const uint32_t* vtoff;
+  const int32_t* seq_lens;
+  float scale_log2;
+  uint16_t* out;
+  float* part;
+  uint32_t* counters;
+};
+
+struct DenseDecodeArgs {
+  const uint16_t* q;
+  int32_t Hq, Hkv, splits;
+  int64_t t_stride;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* seq_lens;
+  float scale_log2;
+  uint16_t* out;
+  float* part;
+  uint32_t* counters;
+};
+
+// Workspace layout: [counters: batch*Hkv u32, padded to 256 B][partials].
+inline uint64_t workspace_counter_bytes(int64_t batch, int64_t hkv) {
+  return (uint64_t)((batch * hkv * 4 + 255) / 256 * 256);
+}
+inline uint64_t workspace_partial_bytes(int64_t batch, int64_t hq, int64_t splits) {
+  return (uint64_t)(batch * hq * splits * kPartStride * 4);
+}
+
+hipError_t launch_prune_compress(const mustafar_kv_t& dst, const uint16_t* dense, int64_t t_stride,
+                                 const int32_t* seq_lens, hipStream_t stream);
+hipError_t launch_append(const mustafar_kv_t& k, const mustafar_kv_t& v, const uint16_t* k_new,
+                         const uint16_t* v_new, int32_t* seq_lens, uint32_t* status,
+                         hipStream_t stream);
+hipError_t launch_decode_sparse(const SparseDecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_decode_dense(const DenseDecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_zero_u32(uint32_t* p, uint64_t n, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t stream);
+
+}  // namespace mustafar

@@ -1,0 +1,45 @@
+// Small kernels: workspace clearing and the HBM stream-read probe.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace mustafar {
+namespace {
+
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, uint64_t n) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (uint64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// Each block streams contiguous 4 KiB pages with coalesced 16 B loads; the XOR
+// of everything read goes to *sink so the loads cannot be removed.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf,
+                                                          uint64_t pages, uint32_t* sink) {
+  uint32_t x = 0;
+  for (uint64_t pg = blockIdx.x; pg < pages; pg += gridDim.x) {
+    const u32x4 v = __builtin_nontemporal_load(buf + pg * 256 + threadIdx.x);
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (x == 0x9E3779B9u) atomicXor(sink, x);  // practically never taken
+}
+
+}  // namespace
+
+hipError_t launch_zero_u32(uint32_t* p, uint64_t n, hipStream_t stream) {
+  uint64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t stream) {
+  const uint64_t pages = bytes / 4096;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(256 * 32), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(buf), pages, sink);
+  return hipGetLastError();
+}
+
+}  // namespace mustafar
