@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the MUSTAFAR decode step on one MI355X.
+
+Workload: one Llama-3-8B-shaped attention layer -- batch 8, 32 query heads over
+8 kv heads, head_dim 128, 32768 cached tokens per sequence, key and value caches
+pruned per token to 70% sparsity (38 of 128 channels kept) and bitmap-compressed.
+Inputs are seeded synthetic data (keys N(0,1) with 4 outlier channels x10 per
+kv head; values and queries N(0,1)), generated on the GPU.
+
+A step is one pass of the decode hot path: the new key and value row of every
+(sequence, kv head) is pruned and appended to the compressed caches
+(mustafar_append_token), then decode attention runs over the compressed caches
+(mustafar_decode_attn).  `value` is compressed key+value bytes read per step
+divided by the wall time of the timed steps (GB/s).
+
+Also reported: the decode kernel's own rate against the 8 TB/s HBM peak
+(`roofline`, from HIP events on the launch stream), the dense fp16 comparison
+kernel at batch 8 and batch 6, the prefill prune+compress rate, the measured
+stream-read rate of the same device, and the CPU oracle timed on one full
+decode step (`cpu_baseline`).
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "sparse decode-attn GB/s (% HBM peak) + speedup vs dense fp16, Llama-3-8B shape 70%"
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SOURCES = ["decode_sparse.hip", "merge.hpp", "device_common.hpp", "kernels.hpp"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "unstructured_sparse_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, "decode_sparse_llama3_8b_layer_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path shards by (batch, kv head) with no exchange; see the sharding note "
+              "in the design document)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import unstructured_sparse_kv_amd as usk
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    cfg = synth.CONFIGS["llama3_8b_layer"]
+    B, Hq, Hkv, T0, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.T, cfg.d
+    keep = usk.keep_from_sparsity(cfg.sparsity)
+    total_steps = args.warmup + args.steps + 1
+    cap = (T0 + total_steps + 63) // 64 * 64
+    scale = 1.0 / math.sqrt(d)
+
+    log(f"generating synthetic caches B={B} Hkv={Hkv} T={T0} (capacity {cap}) on the GPU")
+    K, V, _, _ = synth.make_inputs(cfg, device=dev, T=cap)  # rows T0..cap-1 are spare room
+    seq_d = torch.full((B,), T0, dtype=torch.int32, device=dev)
+    steps_in = [synth.step_inputs(cfg, i, device=dev) for i in range(total_steps)]
+    torch.cuda.synchronize()
+
+    # ---- prefill prune + compress (timed with events)
+    kc = usk.CompressedKV(B, Hkv, keep, cap, dev)
+    vc = usk.CompressedKV(B, Hkv, keep, cap, dev)
+    usk.prune_compress(kc, K, seq_d)
+    usk.prune_compress(vc, V, seq_d)
+    torch.cuda.synchronize()
+    pre = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        usk.prune_compress(kc, K, seq_d)
+        usk.prune_compress(vc, V, seq_d)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pre.append(e0.elapsed_time(e1) * 1e-3)
+    seq_host = np.full(B, T0, np.int32)
+    comp_bytes0 = kc.used_bytes(seq_host) + vc.used_bytes(seq_host)
+    dense_bytes0 = 2 * B * Hkv * T0 * d * 2
+    prefill_s = median(pre)
+    log(f"prefill prune+compress K and V: {prefill_s * 1e6:.1f} us "
+        f"({(dense_bytes0 + comp_bytes0) / prefill_s / 1e9:.0f} GB/s moved)")
+
+    ws = usk.make_workspace(B, Hq, Hkv, cap)
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(i):
+        kn, vn, q = steps_in[i]
+        usk.append_token(kc, vc, kn, vn, seq_d, status)
+        usk.decode_attn(q, kc, vc, seq_d, cap, scale, out, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed steps: wall clock around all of them, events around each decode launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        kn, vn, q = steps_in[args.warmup + j]
+        usk.append_token(kc, vc, kn, vn, seq_d, status)
+        evs[j][0].record(stream)
+        usk.decode_attn(q, kc, vc, seq_d, cap, scale, out, ws)
+        evs[j][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert status.item() == 0
+    step_bytes, kern_s = [], []
+    for j in range(args.steps):
+        L = T0 + args.warmup + j + 1
+        sh = np.full(B, L, np.int32)
+        step_bytes.append(kc.used_bytes(sh) + vc.used_bytes(sh))
+        kern_s.append(evs[j][0].elapsed_time(evs[j][1]) * 1e-3)
+    value = sum(step_bytes) / wall / 1e9
+    ms_per_step = wall / args.steps * 1e3
+    per_launch_bytes = sum(step_bytes) / len(step_bytes)
+    kern_avg = sum(kern_s) / len(kern_s)
+    achieved = per_launch_bytes / kern_avg / 1e9
+    log(f"step: {ms_per_step * 1e3:.1f} us wall ({value:.0f} GB/s); decode kernel avg "
+        f"{kern_avg * 1e6:.1f} us = {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
+    # ---- decode with caches flushed from the last-level caches before every launch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    kn, vn, q_last = steps_in[-1]
+    flushed = []
+    for _ in range(10):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        usk.decode_attn(q_last, kc, vc, seq_d, cap, scale, out, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        flushed.append(e0.elapsed_time(e1) * 1e-3)
+    flushed_s = median(flushed)
+
+    # ---- achievable read rate (stream-read probe) and write rate (workspace clear)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    reads = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        usk.probe_stream_read(flush, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reads.append(flush.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    stream_read_gbs = max(reads)
+    usk.lib().mustafar_decode_workspace_init(flush.data_ptr(), flush.numel(), stream.cuda_stream)
+    del flush
+    log(f"stream-read probe: {stream_read_gbs:.0f} GB/s; decode with flushed caches "
+        f"{flushed_s * 1e6:.1f} us")
+
+    # ---- dense fp16 comparison kernel (same cache data, unpruned), batch 8 and batch 6
+    dense = {}
+    if not args.no_dense:
+        seq_dense = torch.full((B,), T0, dtype=torch.int32, device=dev)
+        q8 = steps_in[-1][2]
+        for bsz in (8, 6):
+            wsd = usk.make_workspace(bsz, Hq, Hkv, T0)
+            outd = torch.empty((bsz, Hq, d), dtype=torch.float16, device=dev)
+            qb = q8[:bsz].contiguous()
+            for _ in range(3):
+                usk.dense_decode_attn(qb, K[:bsz], V[:bsz], seq_dense[:bsz], T0, scale, outd, wsd)
+            ts = []
+            for _ in range(10):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                usk.dense_decode_attn(qb, K[:bsz], V[:bsz], seq_dense[:bsz], T0, scale, outd, wsd)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            dense[bsz] = median(ts)
+            log(f"dense fp16 decode B={bsz}: {dense[bsz] * 1e6:.1f} us "
+                f"({bsz * Hkv * T0 * 512 / dense[bsz] / 1e9:.0f} GB/s)")
+
+    # ---- parity of the last decode step and the CPU oracle on that full step
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        usk.decode_attn(q_last, kc, vc, seq_d, cap, scale, out, ws)
+        torch.cuda.synchronize()
+        L = int(seq_d[0].item())
+        sh = np.full(B, L, np.int32)
+
+        def host_copy(c):
+            bm, vals, toff = c.views()
+            h = oracle.Compressed(B, Hkv, cap, d, keep)
+            h.bitmaps[...] = bm.cpu().numpy().view(np.uint64)
+            h.values[...] = vals.cpu().numpy().view(np.uint16)
+            h.tile_off[...] = toff.cpu().numpy().view(np.uint32)
+            return h
+
+        kh, vh = host_copy(kc), host_copy(vc)
+        nthreads = min(16, oracle.hardware_threads())
+        log(f"CPU oracle: one full decode step ({B * Hq} (batch, q head) pairs, {L} tokens) "
+            f"on {nthreads} threads")
+        c0 = time.perf_counter()
+        ref = oracle.attention_compressed(q_last.cpu(), kh, vh, sh, scale, nthreads=nthreads)
+        cpu_s = time.perf_counter() - c0
+        cpu_bytes = kc.used_bytes(sh) + vc.used_bytes(sh)
+        got = out.float().cpu().numpy().astype(np.float64)
+        parity = {"max_abs": float(np.abs(got - ref).max()),
+                  "rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref))}
+        cpu = {"value": round(cpu_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": nthreads,
+               "kind": "oracle",
+               "sample": f"one full decode step of the workload: attention for all {B * Hq} "
+                         f"(batch, q head) pairs over the {L}-token compressed caches "
+                         f"({cpu_bytes} compressed bytes), {cpu_s:.2f} s wall"}
+        log(f"CPU oracle: {cpu_s:.2f} s ({cpu['value']} GB/s); GPU vs oracle max_abs="
+            f"{parity['max_abs']:.2e} rel_l2={parity['rel_l2']:.2e}")
+
+    decode_s = median(kern_s)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in, f32 accumulate",
+        "data": "synthetic (seeded; keys N(0,1) with 4 outlier channels x10 per kv head, values "
+                "and queries N(0,1))",
+        "config": {"workload": "llama3_8b_layer: Llama-3-8B-shaped attention layer, decode step = "
+                               "append one token per (sequence, kv head) + sparse decode attention",
+                   "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "seq_len": T0,
+                   "sparsity": cfg.sparsity, "keep": keep, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "decode_sparse_kernel<4,48> (mustafar_decode_attn)",
+                     "bytes_per_launch": int(per_launch_bytes),
+                     "avg_launch_us": round(kern_avg * 1e6, 2)},
+        "cpu_baseline": cpu,
+        "extra": {
+            "compressed_kv_bytes": int(comp_bytes0),
+            "dense_kv_bytes": int(dense_bytes0),
+            "compressed_over_dense": round(comp_bytes0 / dense_bytes0, 4),
+            "pages_ratio_at_70pct": 0.45,
+            "decode_us_median": round(decode_s * 1e6, 2),
+            "decode_us_flushed_median": round(flushed_s * 1e6, 2),
+            "decode_gbs_flushed": round(per_launch_bytes / flushed_s / 1e9, 1),
+            "stream_read_gbs": round(stream_read_gbs, 1),
+            "decode_frac_of_stream_read": round(achieved / stream_read_gbs, 4),
+            "prefill_compress_us": round(prefill_s * 1e6, 1),
+            "prefill_gbs_moved": round((dense_bytes0 + comp_bytes0) / prefill_s / 1e9, 1),
+            "parity_last_step": parity,
+        },
+    }
+    if dense:
+        res["extra"].update({
+            "dense_us_b8": round(dense[8] * 1e6, 2),
+            "dense_us_b6": round(dense[6] * 1e6, 2),
+            "speedup_vs_dense_b8": round(dense[8] / decode_s, 3),
+            "tokens_per_s_ratio_sparse_b8_vs_dense_b6": round((8 / decode_s) / (6 / dense[6]), 3),
+            "pages_tokens_per_s_ratio_b8_vs_b6": 2.23,
+        })
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -76,7 +76,7 @@ int decode_common_checks(const uint16_t* q, int32_t hq, int32_t batch, int32_t h
   if (!isfinite(scale)) return MUSTAFAR_EINVAL;
   if (batch > 65535 || hkv > 65535) return MUSTAFAR_EINVAL;  // grid z and y
   const int sp = splits ? splits : auto_splits(batch, hkv, max_seq_len);
-  const uint64_t need = workspace_counter_bytes(batch, hkv) + workspace_partial_bytes(batch, hq, sp);
+  const uint64_t need = workspace_partial_bytes(batch, hq, sp);
   if (ws_bytes < need) return MUSTAFAR_ENOSPACE;
   *splits_out = sp;
   return MUSTAFAR_OK;
@@ -173,8 +173,7 @@ int mustafar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
   if (head_dim != kHeadDim) return MUSTAFAR_EUNSUPPORTED;
   if (num_q_heads % num_kv_heads != 0) return MUSTAFAR_EINVAL;
   const int sp = splits ? splits : auto_splits(batch, num_kv_heads, max_seq_len);
-  *bytes = workspace_counter_bytes(batch, num_kv_heads) +
-           workspace_partial_bytes(batch, num_q_heads, sp);
+  *bytes = workspace_partial_bytes(batch, num_q_heads, sp);
   return MUSTAFAR_OK;
 }
 
@@ -215,10 +214,10 @@ int mustafar_decode_attn(const uint16_t* q, int32_t num_q_heads, const mustafar_
   a.vtoff = v->tile_offsets;
   a.seq_lens = seq_lens;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
-  a.out = out;
-  a.counters = (uint32_t*)workspace;
-  a.part = (float*)((char*)workspace + workspace_counter_bytes(k->batch, k->num_kv_heads));
-  return launched(launch_decode_sparse(a, k->batch, (hipStream_t)stream));
+  a.part = (float*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = launched(launch_decode_sparse(a, k->batch, st)))) return rc;
+  return launched(launch_decode_reduce(a.part, k->batch, num_q_heads, k->num_kv_heads, sp, out, st));
 }
 
 int mustafar_dense_decode_attn(const uint16_t* q, int32_t num_q_heads, const uint16_t* k,
@@ -245,10 +244,10 @@ int mustafar_dense_decode_attn(const uint16_t* q, int32_t num_q_heads, const uin
   a.v = v;
   a.seq_lens = seq_lens;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  a.out = out;
-  a.counters = (uint32_t*)workspace;
-  a.part = (float*)((char*)workspace + workspace_counter_bytes(batch, num_kv_heads));
-  return launched(launch_decode_dense(a, batch, (hipStream_t)stream));
+  a.part = (float*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = launched(launch_decode_dense(a, batch, st)))) return rc;
+  return launched(launch_decode_reduce(a.part, batch, num_q_heads, num_kv_heads, sp, out, st));
 }
 
 int mustafar_probe_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {

@@ -32,7 +32,6 @@ struct DenseCfg {
 template <int G>
 __global__ __launch_bounds__(kDecodeBlock) void decode_dense_kernel(DenseDecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ int last_flag;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int unit = b * a.Hkv + h;
   const int wave = wave_uniform((int)(threadIdx.x / kWave));
@@ -76,17 +75,25 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_dense_kernel(DenseDecodeA
   for (int tile = tb; tile < te; ++tile) {
     const int row0 = tile * kTile;
     const int nvalid = min(kTile, T - row0);
+    // the whole tile's loads first: 16 x 16 B of keys, 16 x 16 B of values per lane
+    uint4 ka[16], vr[16];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        ka[4 * mb + kb] = buf_load16(krs, (uint32_t)(row0 + 16 * mb + l16) * (kHeadDim * 2) +
+                                              (32 * kb + 8 * grp) * 2);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      vr[i] = buf_load16(vrs, (uint32_t)(row0 + 4 * i + grp) * (kHeadDim * 2) + 16 * l16);
     floatx4 cs[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       cs[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const uint32_t rowoff = (uint32_t)(row0 + 16 * mb + l16) * (kHeadDim * 2);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint4 x = buf_load16(krs, rowoff + (32 * kb + 8 * grp) * 2);
-        cs[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, x), bq[kb],
-                                                        cs[mb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < 4; ++kb)
+        cs[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ka[4 * mb + kb]),
+                                                        bq[kb], cs[mb], 0, 0, 0);
     }
     // online softmax for head l16 over this lane's 16 rows, then across lane groups
     float sv[16];
@@ -124,13 +131,12 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_dense_kernel(DenseDecodeA
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[g][e] *= al[g];
-    // P.V
-#pragma unroll 4
+    // P.V on the vector units
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 4 * i + (int)grp;
       if (r < nvalid) {
-        const uint4 x = buf_load16(vrs, (uint32_t)(row0 + r) * (kHeadDim * 2) + 16 * l16);
-        const half8 v = __builtin_bit_cast(half8, x);
+        const half8 v = __builtin_bit_cast(half8, vr[i]);
         float pg[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) pg[g] = p_lds[r * G + g];
@@ -169,8 +175,7 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_dense_kernel(DenseDecodeA
       for (int e = 0; e < 8; ++e) lds_acc[(wave * G + g) * kHeadDim + 8 * lane + e] = acc[g][e];
   }
   __syncthreads();
-  finish_split<G>(lds_m, lds_l, lds_acc, &last_flag, unit, b, h, a.Hq, a.splits, s, a.part,
-                  a.counters, a.out);
+  store_split_partial<G>(lds_m, lds_l, lds_acc, G * kHeadDim, kHeadDim, unit, a.splits, s, a.part);
 }
 
 template <int G>

@@ -23,9 +23,7 @@ struct SparseDecodeArgs {
   const uint32_t* vtoff;
   const int32_t* seq_lens;
   float scale_log2;
-  uint16_t* out;
   float* part;
-  uint32_t* counters;
 };
 
 struct DenseDecodeArgs {
@@ -36,15 +34,10 @@ struct DenseDecodeArgs {
   const uint16_t* v;
   const int32_t* seq_lens;
   float scale_log2;
-  uint16_t* out;
   float* part;
-  uint32_t* counters;
 };
 
-// Workspace layout: [counters: batch*Hkv u32, padded to 256 B][partials].
-inline uint64_t workspace_counter_bytes(int64_t batch, int64_t hkv) {
-  return (uint64_t)((batch * hkv * 4 + 255) / 256 * 256);
-}
+// Workspace: the split partials, [batch][Hkv][splits][G][kPartStride] fp32.
 inline uint64_t workspace_partial_bytes(int64_t batch, int64_t hq, int64_t splits) {
   return (uint64_t)(batch * hq * splits * kPartStride * 4);
 }
@@ -56,6 +49,8 @@ hipError_t launch_append(const mustafar_kv_t& k, const mustafar_kv_t& v, const u
                          hipStream_t stream);
 hipError_t launch_decode_sparse(const SparseDecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_decode_dense(const DenseDecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_decode_reduce(const float* part, int batch, int hq, int hkv, int splits,
+                                uint16_t* out, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, uint64_t n, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t stream);
 

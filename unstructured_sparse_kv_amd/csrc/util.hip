@@ -25,7 +25,43 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   if (x == 0x9E3779B9u) atomicXor(sink, x);  // practically never taken
 }
 
+// Merge the split partials of one (batch, q head): block (b*Hq + hq), thread =
+// channel.  M = max m_s, L = sum l_s 2^(m_s - M), out = sum acc_s 2^(m_s - M) / L
+// (0 for an empty sequence).
+__global__ __launch_bounds__(kHeadDim) void decode_reduce_kernel(const float* __restrict__ part,
+                                                                 int hq_total, int g_size,
+                                                                 int splits,
+                                                                 uint16_t* __restrict__ out) {
+  const int bq = blockIdx.x;
+  const int b = bq / hq_total, hq = bq % hq_total;
+  const int hkv = hq_total / g_size;
+  const int h = hq / g_size, g = hq % g_size;
+  const int unit = b * hkv + h;
+  const int c = threadIdx.x;
+  const float ninf = -__builtin_inff();
+  const float* pu = part + ((int64_t)unit * splits * g_size + g) * kPartStride;
+  const int64_t sstride = (int64_t)g_size * kPartStride;
+  float M = ninf;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, pu[s * sstride]);
+  float A = 0.f, L = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* ps = pu + s * sstride;
+    const float ms = ps[0];
+    const float f = (ms == ninf) ? 0.f : exp2f(ms - M);
+    A += ps[2 + c] * f;
+    L += ps[1] * f;
+  }
+  out[(int64_t)bq * kHeadDim + c] = float_to_half_bits(L > 0.f ? A / L : 0.f);
+}
+
 }  // namespace
+
+hipError_t launch_decode_reduce(const float* part, int batch, int hq, int hkv, int splits,
+                                uint16_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3(batch * hq), dim3(kHeadDim), 0, stream, part, hq,
+                     hq / hkv, splits, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_zero_u32(uint32_t* p, uint64_t n, hipStream_t stream) {
   uint64_t blocks = (n + 255) / 256;
