@@ -167,10 +167,10 @@ int mustafar_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
                                     uint64_t *bytes);
 
 /*
- * Prepare a workspace (device, `bytes` long) for the decode calls: clears the
- * per-(batch, kv head) completion counters.  Call once after allocating it;
- * each decode call leaves the counters cleared again.  Calls that share a
- * workspace must be ordered (same stream); overlapping ones race.
+ * Clear a decode workspace (device, `bytes` long, a multiple of 4).  The decode
+ * calls need no particular workspace contents; clearing is only for callers
+ * that want deterministic memory.  Calls that share a workspace must be
+ * ordered (same stream); overlapping ones race.
  */
 int mustafar_decode_workspace_init(void *workspace, uint64_t bytes, void *stream);
 
@@ -191,10 +191,12 @@ int mustafar_decode_workspace_init(void *workspace, uint64_t bytes, void *stream
  *   scale        softmax scale (1/sqrt(128) for standard attention).
  *   splits       number of sequence splits per (batch, kv head); 0 = automatic.
  *   out  (device) uint16 [batch][num_q_heads][128] fp16 bits (round to nearest).
- *   workspace    (device) from mustafar_decode_workspace_bytes, initialised once
- *                with mustafar_decode_workspace_init.
- * Arithmetic: fp16 inputs, fp32 products and accumulation, fp32 online softmax
- * per split and a cross-split merge.  One kernel launch.
+ *   workspace    (device) at least mustafar_decode_workspace_bytes long; it holds
+ *                the per-split partial states between the two launches.
+ * Arithmetic: fp16 inputs; scores with fp32 products and accumulation; fp32
+ * online softmax per split; P.V with the probabilities rounded to fp16 pairs
+ * and fp32 accumulation (v_dot2_f32_f16); a cross-split merge in fp32.
+ * Two kernel launches on `stream`: the split kernel and the merge.
  */
 int mustafar_decode_attn(const uint16_t *q, int32_t num_q_heads, const mustafar_kv_t *k,
                          const mustafar_kv_t *v, const int32_t *seq_lens, int32_t max_seq_len,
@@ -205,7 +207,7 @@ int mustafar_decode_attn(const uint16_t *q, int32_t num_q_heads, const mustafar_
  * The same attention over dense, unpruned fp16 caches: the comparison
  * baseline (the pages compare against dense attention, [Summary] "Key results"
  * and "Experimental setup").  q.K^T runs on the matrix cores (MFMA), P.V and
- * the softmax on the vector units.
+ * the softmax on the vector units (fp32); two launches like mustafar_decode_attn.
  *
  *   k, v (device) uint16 [batch][num_kv_heads][t_stride][128] fp16 bits; rows
  *        t < min(seq_lens[b], t_stride) are attended.

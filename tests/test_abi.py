@@ -131,8 +131,8 @@ def test_workspace_sizing_and_auto_splits():
     rc, n = _ws_bytes(8, 32, 8, 32768)
     sp = L.mustafar_decode_auto_splits(8, 8, 32768)
     assert rc == 0 and 1 <= sp <= 1024
-    assert n == ((8 * 8 * 4 + 255) // 256 * 256) + 8 * 32 * sp * 132 * 4
-    assert _ws_bytes(8, 32, 8, 32768, splits=4)[1] == 256 + 8 * 32 * 4 * 132 * 4
+    assert n == 8 * 32 * sp * 132 * 4  # one (m, l, acc[128], pad) partial per (b, q head, split)
+    assert _ws_bytes(8, 32, 8, 32768, splits=4)[1] == 8 * 32 * 4 * 132 * 4
     assert _ws_bytes(8, 30, 8, 100)[0] == usk.MUSTAFAR_EINVAL
     assert _ws_bytes(8, 32, 8, 100, hd=96)[0] == usk.MUSTAFAR_EUNSUPPORTED
     assert _ws_bytes(8, 32, 8, 100, splits=5000)[0] == usk.MUSTAFAR_EINVAL
