@@ -193,15 +193,36 @@ int mustafar_decode_workspace_init(void *workspace, uint64_t bytes, void *stream
  *   out  (device) uint16 [batch][num_q_heads][128] fp16 bits (round to nearest).
  *   workspace    (device) at least mustafar_decode_workspace_bytes long; it holds
  *                the per-split partial states between the two launches.
- * Arithmetic: fp16 inputs; scores with fp32 products and accumulation; fp32
- * online softmax per split; P.V with the probabilities rounded to fp16 pairs
- * and fp32 accumulation (v_dot2_f32_f16); a cross-split merge in fp32.
+ * Arithmetic: fp16 inputs; each 64-row tile's stored entries are decoded
+ * into a dense fp16 tile in LDS and both contractions run on the matrix cores
+ * (v_mfma_f32_16x16x32_f16, fp32 accumulation): scores from the decoded key
+ * tile, P.V with the probabilities rounded to fp16; fp32 online softmax per
+ * split; a cross-split merge in fp32.
  * Two kernel launches on `stream`: the split kernel and the merge.
+ * Errors: MUSTAFAR_EINVAL for null or misaligned pointers (q, out, workspace
+ * 16 B; seq_lens 4 B), shape mismatches between k and v, num_q_heads not a
+ * multiple of num_kv_heads, a non-finite scale or splits outside [0, 1024];
+ * MUSTAFAR_EUNSUPPORTED for a group size other than 1, 2, 4, 8;
+ * MUSTAFAR_ENOSPACE for a workspace smaller than needed; MUSTAFAR_ENODEV,
+ * MUSTAFAR_ELAUNCH from the runtime.  Nothing is launched on an error.
  */
 int mustafar_decode_attn(const uint16_t *q, int32_t num_q_heads, const mustafar_kv_t *k,
                          const mustafar_kv_t *v, const int32_t *seq_lens, int32_t max_seq_len,
                          float scale, int32_t splits, uint16_t *out, void *workspace,
                          uint64_t workspace_bytes, void *stream);
+
+/*
+ * The same operation, arguments and errors as mustafar_decode_attn, computed
+ * on the vector units only: each decoded key entry is multiplied straight into
+ * the G scores of its row (fp32 fma), and P.V accumulates from a channel-major
+ * decoded value tile with the probabilities as fp16 pairs (v_dot2_f32_f16,
+ * fp32 accumulation).  Kept as a second implementation of the same attention
+ * for comparison.
+ */
+int mustafar_decode_attn_valu(const uint16_t *q, int32_t num_q_heads, const mustafar_kv_t *k,
+                              const mustafar_kv_t *v, const int32_t *seq_lens, int32_t max_seq_len,
+                              float scale, int32_t splits, uint16_t *out, void *workspace,
+                              uint64_t workspace_bytes, void *stream);
 
 /*
  * The same attention over dense, unpruned fp16 caches: the comparison

@@ -18,11 +18,16 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _decode(q, kc, vc, seq_dev, max_len, splits=0):
+# The two sparse decode kernels (matrix-core and vector-unit) compute the same
+# attention; every sparse case runs both.
+SPARSE = {"mfma": usk.decode_attn, "valu": usk.decode_attn_valu}
+
+
+def _decode(q, kc, vc, seq_dev, max_len, splits=0, variant="mfma"):
     B, Hq = q.shape[0], q.shape[1]
     ws = usk.make_workspace(B, Hq, kc.num_kv_heads, max_len, splits)
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device=q.device)
-    usk.decode_attn(q, kc, vc, seq_dev, max_len, SCALE, out, ws, splits)
+    SPARSE[variant](q, kc, vc, seq_dev, max_len, SCALE, out, ws, splits)
     torch.cuda.synchronize()
     return out
 
@@ -52,8 +57,10 @@ def test_tiny_end_to_end(gpu):
     ko, vo = oracle.compress(K, seq, keep, cfg.T), oracle.compress(V, seq, keep, cfg.T)
     assert_compressed_equal(kc, ko, seq)
     assert_compressed_equal(vc, vo, seq)
-    out = _decode(q.to(gpu), kc, vc, seq_d, cfg.T)
-    assert_attn_close(_f64(out), oracle.attention_compressed(q, ko, vo, seq, SCALE), "tiny sparse")
+    ref = oracle.attention_compressed(q, ko, vo, seq, SCALE)
+    for variant in SPARSE:
+        out = _decode(q.to(gpu), kc, vc, seq_d, cfg.T, variant=variant)
+        assert_attn_close(_f64(out), ref, f"tiny sparse {variant}")
     outd = _dense(q.to(gpu), K.to(gpu), V.to(gpu), seq_d, cfg.T)
     assert_attn_close(_f64(outd), oracle.attention_dense(q, K, V, seq, SCALE), "tiny dense")
 
@@ -121,9 +128,10 @@ def test_keep_sweep(gpu, kk, kv):
     assert_compressed_equal(kc, ko, seq)
     assert_compressed_equal(vc, vo, seq)
     ref = oracle.attention_compressed(q, ko, vo, seq, SCALE)
-    for splits in (0, 1, 3):
-        out = _decode(q.to(gpu), kc, vc, seq_d, 200, splits)
-        assert_attn_close(_f64(out), ref, f"kk={kk} kv={kv} splits={splits}")
+    for variant in SPARSE:
+        for splits in (0, 1, 3):
+            out = _decode(q.to(gpu), kc, vc, seq_d, 200, splits, variant)
+            assert_attn_close(_f64(out), ref, f"kk={kk} kv={kv} splits={splits} {variant}")
 
 
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
@@ -136,9 +144,11 @@ def test_group_sizes(gpu, G):
     seq_d = torch.from_numpy(seq).to(gpu)
     kc = compress_on_gpu(K.to(gpu), seq_d, 38, 384)
     vc = compress_on_gpu(V.to(gpu), seq_d, 38, 384)
-    out = _decode(q.to(gpu), kc, vc, seq_d, 333)
     ko, vo = oracle.compress(K, seq, 38, 384), oracle.compress(V, seq, 38, 384)
-    assert_attn_close(_f64(out), oracle.attention_compressed(q, ko, vo, seq, SCALE), f"sparse G={G}")
+    ref = oracle.attention_compressed(q, ko, vo, seq, SCALE)
+    for variant in SPARSE:
+        out = _decode(q.to(gpu), kc, vc, seq_d, 333, variant=variant)
+        assert_attn_close(_f64(out), ref, f"sparse G={G} {variant}")
     outd = _dense(q.to(gpu), K.to(gpu), V.to(gpu), seq_d, 333)
     assert_attn_close(_f64(outd), oracle.attention_dense(q, K, V, seq, SCALE), f"dense G={G}")
 
@@ -157,8 +167,10 @@ def test_llama2_layer_full(gpu):
     assert_compressed_equal(vc, vo, seq)
     assert kc.used_bytes(seq.numpy()) + vc.used_bytes(seq.numpy()) == \
         2 * oracle.used_bytes(1, 32, seq.numpy(), cfg.T, 128, keep)
-    out = _decode(q.to(gpu), kc, vc, seq_d, cfg.T)
-    assert_attn_close(_f64(out), oracle.attention_compressed(q, ko, vo, seq, SCALE), "llama2 sparse")
+    ref = oracle.attention_compressed(q, ko, vo, seq, SCALE)
+    for variant in SPARSE:
+        out = _decode(q.to(gpu), kc, vc, seq_d, cfg.T, variant=variant)
+        assert_attn_close(_f64(out), ref, f"llama2 sparse {variant}")
     outd = _dense(q.to(gpu), K.to(gpu), V.to(gpu), seq_d, cfg.T)
     assert_attn_close(_f64(outd), oracle.attention_dense(q, K, V, seq, SCALE), "llama2 dense")
 
@@ -188,15 +200,17 @@ def test_llama3_layer_sampled(gpu):
         h = hq // 4
         refd[(b, hq)] = oracle.attention_dense(qcpu[b:b + 1, hq:hq + 1], Kcpu[b:b + 1, h:h + 1],
                                                Vcpu[b:b + 1, h:h + 1], [cfg.T], SCALE)[0, 0]
-    outs = {}
-    for splits in (0, 1, 7, 64):
-        say(f"llama3 layer: sparse decode splits={splits}")
-        out = _decode(q, kc, vc, seq_d, cfg.T, splits)
-        outs[splits] = out.clone()
-        got = np.stack([_f64(out[b, hq]) for b, hq in pairs])
-        assert_attn_close(got, np.stack([ref[p] for p in pairs]), f"llama3 sparse splits={splits}")
-    again = _decode(q, kc, vc, seq_d, cfg.T, 0)
-    assert torch.equal(again, outs[0]), "decode is not deterministic"
+    for variant in SPARSE:
+        outs = {}
+        for splits in (0, 1, 7, 64):
+            say(f"llama3 layer: sparse decode ({variant}) splits={splits}")
+            out = _decode(q, kc, vc, seq_d, cfg.T, splits, variant)
+            outs[splits] = out.clone()
+            got = np.stack([_f64(out[b, hq]) for b, hq in pairs])
+            assert_attn_close(got, np.stack([ref[p] for p in pairs]),
+                              f"llama3 sparse {variant} splits={splits}")
+        again = _decode(q, kc, vc, seq_d, cfg.T, 0, variant)
+        assert torch.equal(again, outs[0]), f"decode ({variant}) is not deterministic"
     say("llama3 layer: dense baseline")
     outd = _dense(q, K, V, seq_d, cfg.T)
     got = np.stack([_f64(outd[b, hq]) for b, hq in pairs])
@@ -218,12 +232,14 @@ def test_ragged_append_sequence(gpu):
     status = torch.zeros(1, dtype=torch.int32, device=gpu)
     ws = usk.make_workspace(cfg.B, cfg.Hq, cfg.Hkv, cap)
     out = torch.empty((cfg.B, cfg.Hq, 128), dtype=torch.float16, device=gpu)
+    outv = torch.empty_like(out)
     pairs = [(0, 0), (5, 13), (9, 30), (15, 7)]
     check_steps = {1, 2, 32, cfg.steps}
     for step in range(1, cfg.steps + 1):
         kn, vn, q = synth.step_inputs(cfg, step - 1, device=gpu)
         usk.append_token(kc, vc, kn, vn, seq_d, status)
         usk.decode_attn(q, kc, vc, seq_d, cap, SCALE, out, ws)
+        usk.decode_attn_valu(q, kc, vc, seq_d, cap, SCALE, outv, ws)
         # the oracle sees the same new rows written into its dense copy
         T_old = seq0 + (step - 1)
         for b in range(cfg.B):
@@ -235,7 +251,7 @@ def test_ragged_append_sequence(gpu):
             assert np.array_equal(seq_d.cpu().numpy(), seq_now)
             say(f"ragged append: step {step} parity")
             qcpu = q.cpu()
-            got, exp = [], []
+            got, gotv, exp = [], [], []
             for b, hq in pairs:
                 h = hq // 4
                 T = int(seq_now[b])
@@ -244,10 +260,12 @@ def test_ragged_append_sequence(gpu):
                 vo = oracle.compress(V[b:b + 1, h:h + 1, :T].cpu(), s1, keep, cap)
                 exp.append(oracle.attention_compressed(qcpu[b:b + 1, hq:hq + 1], ko, vo, s1, SCALE)[0, 0])
                 got.append(_f64(out[b, hq]))
+                gotv.append(_f64(outv[b, hq]))
                 if step == cfg.steps:
                     assert_compressed_equal(kc, ko, seq_now, [(b, h)], [(0, 0)])
                     assert_compressed_equal(vc, vo, seq_now, [(b, h)], [(0, 0)])
             assert_attn_close(np.stack(got), np.stack(exp), f"ragged append step {step}")
+            assert_attn_close(np.stack(gotv), np.stack(exp), f"ragged append step {step} valu")
     assert status.item() == 0
 
 
@@ -271,18 +289,19 @@ def test_edge_cases(gpu):
     assert_compressed_equal(vc, vo, seq_c)
     # canaries around the output
     ws = usk.make_workspace(B, Hq, Hkv, cap)
-    buf = torch.full((B * Hq * 128 + 2 * 256,), 0x7E01, dtype=torch.int16, device=gpu)  # NaN pattern
-    out = buf[256:256 + B * Hq * 128].view(torch.float16).view(B, Hq, 128)
-    usk.decode_attn(q.to(gpu), kc, vc, seq_d, cap, SCALE, out, ws)
-    torch.cuda.synchronize()
-    assert (buf[:256] == 0x7E01).all() and (buf[-256:] == 0x7E01).all(), "canary overwritten"
     ref = oracle.attention_compressed(q, ko, vo, seq_c, SCALE)
-    assert not out[0].any(), "empty sequence must give zeros"
-    assert_attn_close(_f64(out), ref, "edge cases")
-    # T = 1: the output is the stored first value row for every head of the group
     v0 = oracle.decompress(vo, seq_c)[1, :, 0].view(np.float16).astype(np.float64)
-    for hq in range(Hq):
-        assert np.array_equal(_f64(out[1, hq]), v0[hq // 2].astype(np.float16).astype(np.float64))
+    for variant, fn in SPARSE.items():
+        buf = torch.full((B * Hq * 128 + 2 * 256,), 0x7E01, dtype=torch.int16, device=gpu)  # NaN bits
+        out = buf[256:256 + B * Hq * 128].view(torch.float16).view(B, Hq, 128)
+        fn(q.to(gpu), kc, vc, seq_d, cap, SCALE, out, ws)
+        torch.cuda.synchronize()
+        assert (buf[:256] == 0x7E01).all() and (buf[-256:] == 0x7E01).all(), "canary overwritten"
+        assert not out[0].any(), "empty sequence must give zeros"
+        assert_attn_close(_f64(out), ref, f"edge cases {variant}")
+        # T = 1: the output is the stored first value row for every head of the group
+        for hq in range(Hq):
+            assert np.array_equal(_f64(out[1, hq]), v0[hq // 2].astype(np.float16).astype(np.float64))
     # append at capacity: status bit, caches and lengths unchanged
     full = torch.tensor([cap, cap, cap, cap], dtype=torch.int32, device=gpu)
     status = torch.zeros(1, dtype=torch.int32, device=gpu)

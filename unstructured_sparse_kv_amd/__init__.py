@@ -27,8 +27,8 @@ EXPORTS = (
     "mustafar_status_str", "mustafar_keep_from_sparsity", "mustafar_kv_alloc_bytes",
     "mustafar_kv_used_bytes", "mustafar_prune_compress", "mustafar_append_token",
     "mustafar_decode_auto_splits", "mustafar_decode_workspace_bytes",
-    "mustafar_decode_workspace_init", "mustafar_decode_attn", "mustafar_dense_decode_attn",
-    "mustafar_probe_stream_read",
+    "mustafar_decode_workspace_init", "mustafar_decode_attn", "mustafar_decode_attn_valu",
+    "mustafar_dense_decode_attn", "mustafar_probe_stream_read",
 )
 
 
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
             "mustafar_decode_workspace_init": (ctypes.c_int, [P, U64, P]),
             "mustafar_decode_attn": (ctypes.c_int, [P, I32, KVP, KVP, P, I32, ctypes.c_float, I32, P,
                                                     P, U64, P]),
+            "mustafar_decode_attn_valu": (ctypes.c_int, [P, I32, KVP, KVP, P, I32, ctypes.c_float,
+                                                         I32, P, P, U64, P]),
             "mustafar_dense_decode_attn": (ctypes.c_int, [P, I32, P, P, I32, I32, I32, I64, P, I32,
                                                           ctypes.c_float, I32, P, P, U64, P]),
             "mustafar_probe_stream_read": (ctypes.c_int, [P, U64, P, P]),
@@ -188,9 +190,18 @@ def make_workspace(batch, num_q_heads, num_kv_heads, max_seq_len, splits=0, devi
 
 def decode_attn(q, k: CompressedKV, v: CompressedKV, seq_lens, max_seq_len: int, scale: float,
                 out, workspace, splits: int = 0, stream=None) -> None:
-    """q, out: [B][Hq][128] fp16 (device)."""
+    """q, out: [B][Hq][128] fp16 (device).  Matrix-core kernel."""
     assert q.is_contiguous() and out.is_contiguous()
     _check("mustafar_decode_attn", lib().mustafar_decode_attn(
+        q.data_ptr(), q.shape[1], k.ref, v.ref, seq_lens.data_ptr(), max_seq_len, scale, splits,
+        out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def decode_attn_valu(q, k: CompressedKV, v: CompressedKV, seq_lens, max_seq_len: int,
+                     scale: float, out, workspace, splits: int = 0, stream=None) -> None:
+    """Same as decode_attn, vector-unit kernel."""
+    assert q.is_contiguous() and out.is_contiguous()
+    _check("mustafar_decode_attn_valu", lib().mustafar_decode_attn_valu(
         q.data_ptr(), q.shape[1], k.ref, v.ref, seq_lens.data_ptr(), max_seq_len, scale, splits,
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
 

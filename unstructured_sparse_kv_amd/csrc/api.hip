@@ -82,6 +82,44 @@ int decode_common_checks(const uint16_t* q, int32_t hq, int32_t batch, int32_t h
   return MUSTAFAR_OK;
 }
 
+typedef hipError_t (*SparseLauncher)(const SparseDecodeArgs&, int, hipStream_t);
+
+int sparse_decode(SparseLauncher launch, const uint16_t* q, int32_t num_q_heads,
+                  const mustafar_kv_t* k, const mustafar_kv_t* v, const int32_t* seq_lens,
+                  int32_t max_seq_len, float scale, int32_t splits, uint16_t* out,
+                  void* workspace, uint64_t workspace_bytes, void* stream) {
+  int rc = check_kv(k);
+  if (rc) return rc;
+  if ((rc = check_kv(v))) return rc;
+  if (k->batch != v->batch || k->num_kv_heads != v->num_kv_heads || k->capacity != v->capacity)
+    return MUSTAFAR_EINVAL;
+  int sp = 0;
+  rc = decode_common_checks(q, num_q_heads, k->batch, k->num_kv_heads, max_seq_len, scale, splits,
+                            out, workspace, workspace_bytes, seq_lens, &sp);
+  if (rc) return rc;
+  if ((rc = check_device())) return rc;
+  SparseDecodeArgs a;
+  a.q = q;
+  a.Hq = num_q_heads;
+  a.Hkv = k->num_kv_heads;
+  a.cap = k->capacity;
+  a.kk = k->keep;
+  a.vk = v->keep;
+  a.splits = sp;
+  a.kbm = k->bitmaps;
+  a.kval = k->values;
+  a.ktoff = k->tile_offsets;
+  a.vbm = v->bitmaps;
+  a.vval = v->values;
+  a.vtoff = v->tile_offsets;
+  a.seq_lens = seq_lens;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  a.part = (float*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = launched(launch(a, k->batch, st)))) return rc;
+  return launched(launch_decode_reduce(a.part, k->batch, num_q_heads, k->num_kv_heads, sp, out, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,36 +226,16 @@ int mustafar_decode_attn(const uint16_t* q, int32_t num_q_heads, const mustafar_
                          const mustafar_kv_t* v, const int32_t* seq_lens, int32_t max_seq_len,
                          float scale, int32_t splits, uint16_t* out, void* workspace,
                          uint64_t workspace_bytes, void* stream) {
-  int rc = check_kv(k);
-  if (rc) return rc;
-  if ((rc = check_kv(v))) return rc;
-  if (k->batch != v->batch || k->num_kv_heads != v->num_kv_heads || k->capacity != v->capacity)
-    return MUSTAFAR_EINVAL;
-  int sp = 0;
-  rc = decode_common_checks(q, num_q_heads, k->batch, k->num_kv_heads, max_seq_len, scale, splits,
-                            out, workspace, workspace_bytes, seq_lens, &sp);
-  if (rc) return rc;
-  if ((rc = check_device())) return rc;
-  SparseDecodeArgs a;
-  a.q = q;
-  a.Hq = num_q_heads;
-  a.Hkv = k->num_kv_heads;
-  a.cap = k->capacity;
-  a.kk = k->keep;
-  a.vk = v->keep;
-  a.splits = sp;
-  a.kbm = k->bitmaps;
-  a.kval = k->values;
-  a.ktoff = k->tile_offsets;
-  a.vbm = v->bitmaps;
-  a.vval = v->values;
-  a.vtoff = v->tile_offsets;
-  a.seq_lens = seq_lens;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
-  a.part = (float*)workspace;
-  hipStream_t st = (hipStream_t)stream;
-  if ((rc = launched(launch_decode_sparse(a, k->batch, st)))) return rc;
-  return launched(launch_decode_reduce(a.part, k->batch, num_q_heads, k->num_kv_heads, sp, out, st));
+  return sparse_decode(launch_decode_sparse, q, num_q_heads, k, v, seq_lens, max_seq_len, scale,
+                       splits, out, workspace, workspace_bytes, stream);
+}
+
+int mustafar_decode_attn_valu(const uint16_t* q, int32_t num_q_heads, const mustafar_kv_t* k,
+                              const mustafar_kv_t* v, const int32_t* seq_lens, int32_t max_seq_len,
+                              float scale, int32_t splits, uint16_t* out, void* workspace,
+                              uint64_t workspace_bytes, void* stream) {
+  return sparse_decode(launch_decode_sparse_valu, q, num_q_heads, k, v, seq_lens, max_seq_len,
+                       scale, splits, out, workspace, workspace_bytes, stream);
 }
 
 int mustafar_dense_decode_attn(const uint16_t* q, int32_t num_q_heads, const uint16_t* k,

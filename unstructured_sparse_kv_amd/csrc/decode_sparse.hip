@@ -1,6 +1,7 @@
 // Decode-step attention computed directly over the bitmap-compressed key and
 // value caches ([Summary] "Approach": a custom attention kernel over the bitmap
-// format; [Abstract]; [README] "Part III": batched sparse attention kernel).
+// format; [Abstract]; [README] "Part III": batched sparse attention kernel),
+// vector-unit-only variant (mustafar_decode_attn_valu).
 //
 // Grid (splits, Hkv, B); 4 waves per block.  The 64-row tiles of a
 // (batch, kv head) are divided among the splits * 4 waves; each wave keeps an
@@ -28,186 +29,38 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "merge.hpp"
+#include "decode_walk.hpp"
 
 namespace mustafar {
 namespace {
 
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-constexpr int kTRowBytes = 144;  // one channel row of the value tile: 64 fp16 + 16 B pad
-constexpr int kTRows = 129;      // 128 channels + a dump row for lanes past their last entry
+constexpr int kTRowShift = 7;     // one channel row of the value tile: 64 fp16 = 128 B
+constexpr uint32_t kTRowBytes = 1u << kTRowShift;
+constexpr int kTRows = 129;       // 128 channels + a dump row for lanes past their last entry
 
 template <int G>
 struct SparseCfg {
   static constexpr int kQBytes = ((129 * 2 * G) + 15) / 16 * 16;  // q[c][g] fp16, c = 128 is zero
-  static constexpr int kTileBytes = kTRows * kTRowBytes;
-  static constexpr int kP2Bytes = 32 * G * 4;                     // p pairs, [pair][g] fp16x2
+  static constexpr uint32_t kQMul = 2 * G;  // bytes per channel of the q table
+  static constexpr int kTileBytes = kTRows << kTRowShift;
+  // p pairs: 8 blocks of 4 row pairs; block stride (G | 1) * 4 dwords keeps the
+  // 8 blocks on distinct banks when lanes read different blocks
+  static constexpr int kP2Block = 4 * (G | 1);
+  static constexpr int kP2Bytes = 8 * kP2Block * 4;
   static constexpr int kWaveBytes = (kTileBytes + kP2Bytes + 15) / 16 * 16;
   static constexpr int kMergeBytes = kDecodeWaves * G * (2 + kHeadDim) * 4;
   static constexpr int kLdsBytes =
       kQBytes + (kDecodeWaves * kWaveBytes > kMergeBytes ? kDecodeWaves * kWaveBytes : kMergeBytes);
 };
 
-template <int KMAX>
-struct RowCfg {
-  static constexpr int kChunks = (KMAX / 2 + 1 + 3) / 4;  // 16 B chunks per row (+1 dword for realign)
-  static constexpr int kW = kChunks * 4;                   // dwords of a row in registers
-};
-
-// q[c][g] for the G heads of the group, from the LDS table q_lds[c][g].
-template <int G>
-__device__ __forceinline__ void load_q(const uint16_t* q_lds, uint32_t ch, uint32_t (&qh)[G]) {
-  const uint16_t* p = q_lds + ch * G;
-  if constexpr (G == 1) {
-    qh[0] = p[0];
-  } else if constexpr (G == 2) {
-    const uint32_t x = *reinterpret_cast<const uint32_t*>(p);
-    qh[0] = x & 0xFFFFu;
-    qh[1] = x >> 16;
-  } else if constexpr (G == 4) {
-    const uint2 x = *reinterpret_cast<const uint2*>(p);
-    qh[0] = x.x & 0xFFFFu; qh[1] = x.x >> 16; qh[2] = x.y & 0xFFFFu; qh[3] = x.y >> 16;
-  } else {
-    const uint4 x = *reinterpret_cast<const uint4*>(p);
-    qh[0] = x.x & 0xFFFFu; qh[1] = x.x >> 16; qh[2] = x.y & 0xFFFFu; qh[3] = x.y >> 16;
-    qh[4] = x.z & 0xFFFFu; qh[5] = x.z >> 16; qh[6] = x.w & 0xFFFFu; qh[7] = x.w >> 16;
-  }
-}
-
-template <int KW>
-__device__ __forceinline__ uint32_t value_at(const uint32_t (&row)[KW], int i) {
-  const uint32_t w = row[i >> 1];
-  return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
-// Fast walk over the set bits of a row: every valid row holds exactly n set
-// bits and all four bitmap dwords are non-zero (invalid lanes carry all-ones
-// words and zero values), so the next dword is never empty and no lane runs
-// out before the last step.  f(channel, value bits) is called for each set bit.
-template <int KMAX, int KW, class F>
-__device__ __forceinline__ void walk_fast(const uint32_t (&row)[KW], uint4 w, int n, F&& f) {
-  uint32_t cur = w.x, n1 = w.y, n2 = w.z, n3 = w.w, base = 0;
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i) {
-    if (i < n) {
-      f(base + (uint32_t)__builtin_ctz(cur), value_at(row, i));
-      cur &= cur - 1u;
-      const bool z = (cur == 0u);
-      cur = z ? n1 : cur;
-      n1 = z ? n2 : n1;
-      n2 = z ? n3 : n2;
-      base += z ? 32u : 0u;
-    }
-  }
-}
-
-// General walk: empty dwords are compacted away (each kept dword carries its
-// channel base) and a lane that has used all its set bits reports channel 128
-// (the zero q entry / the dump accumulator); its remaining values are zero.
-template <int KMAX, int KW, class F>
-__device__ __forceinline__ void walk_general(const uint32_t (&row)[KW], uint4 w, int iters, F&& f) {
-  uint32_t cw[4] = {w.x, w.y, w.z, w.w};
-  uint32_t cb[4] = {0u, 32u, 64u, 96u};
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const bool sw = (cw[j] == 0u) && (cw[j + 1] != 0u);
-      const uint32_t a = cw[j], ab = cb[j];
-      cw[j] = sw ? cw[j + 1] : cw[j];
-      cb[j] = sw ? cb[j + 1] : cb[j];
-      cw[j + 1] = sw ? a : cw[j + 1];
-      cb[j + 1] = sw ? ab : cb[j + 1];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) cb[j] = cw[j] ? cb[j] : 128u;
-  uint32_t cur = cw[0], b0 = cb[0], n1 = cw[1], b1 = cb[1], n2 = cw[2], b2 = cb[2], n3 = cw[3],
-           b3 = cb[3];
-#pragma unroll
-  for (int i = 0; i < KMAX; ++i) {
-    if (i < iters) {
-      f(cur ? b0 + (uint32_t)__builtin_ctz(cur) : 128u, value_at(row, i));
-      cur &= cur - 1u;
-      const bool z = (cur == 0u);
-      cur = z ? n1 : cur; b0 = z ? b1 : b0;
-      n1 = z ? n2 : n1; b1 = z ? b2 : b1;
-      n2 = z ? n3 : n2; b2 = z ? b3 : b2;
-      n3 = z ? 0u : n3; b3 = z ? 128u : b3;
-    }
-  }
-}
-
-// Loads dwords of the stored values from half index `start` of the region
-// and shifts them so that row[i] holds values 2i and 2i+1 of the row.
-template <int KW>
-__device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, uint32_t start, int nchunks,
-                                         bool odd_possible, uint32_t (&row)[KW]) {
-  const uint32_t dw0 = start >> 1;
-#pragma unroll
-  for (int j = 0; j < KW / 4; ++j) {
-    uint4 c = make_uint4(0u, 0u, 0u, 0u);
-    if (j < nchunks) c = buf_load16(rs, (dw0 + 4u * j) * 4u);
-    row[4 * j + 0] = c.x; row[4 * j + 1] = c.y; row[4 * j + 2] = c.z; row[4 * j + 3] = c.w;
-  }
-  if (odd_possible) {
-    const bool odd = start & 1u;
-#pragma unroll
-    for (int j = 0; j < KW - 1; ++j)
-      row[j] = odd ? __builtin_amdgcn_alignbit(row[j + 1], row[j], 16u) : row[j];
-  }
-}
-
-// Chunks of 16 B covering n values starting at any half offset (+1 dword slack).
-__device__ __forceinline__ int row_chunks(int n) { return (((n + 1) >> 1) + 1 + 3) >> 2; }
-
-// Zeroes stored values beyond the first `count` of the row.
-template <int KW>
-__device__ __forceinline__ void mask_row(uint32_t (&row)[KW], uint32_t count) {
-#pragma unroll
-  for (int j = 0; j < KW; ++j) {
-    const uint32_t lo_ok = (2u * j < count) ? 0xFFFFu : 0u;
-    const uint32_t hi_ok = (2u * j + 1u < count) ? 0xFFFF0000u : 0u;
-    row[j] &= (lo_ok | hi_ok);
-  }
-}
-
-__device__ __forceinline__ uint32_t pop4(uint4 w) {
-  return __popc(w.x) + __popc(w.y) + __popc(w.z) + __popc(w.w);
-}
-
-// Prepares one side's rows for a walk and reports whether the fast walk applies
-// to the whole wave.  Rows were loaded at the start each would have if every row
-// held exactly `keep` values; when that does not hold the rows are reloaded from
-// their exact starts (prefix sum of the popcounts).
-template <int KW>
-__device__ __forceinline__ bool prepare_rows(__amdgpu_buffer_rsrc_t rs, uint32_t toff, int keep,
-                                             bool valid, bool partial, uint4& bm,
-                                             uint32_t (&row)[KW], int& iters) {
-  const uint32_t pop = pop4(bm);
-  const bool lane_fast = !valid || (pop == (uint32_t)keep && bm.x && bm.y && bm.z && bm.w);
-  if (__ballot(!lane_fast) == 0ull) {
-    if (partial) {
-      if (!valid) bm = make_uint4(~0u, ~0u, ~0u, ~0u);
-#pragma unroll
-      for (int j = 0; j < KW; ++j) row[j] = valid ? row[j] : 0u;
-    }
-    iters = keep;
-    return true;
-  }
-  const uint32_t pc = valid ? pop : 0u;
-  const uint32_t st = toff + wave_excl_scan(pc);
-  iters = (int)wave_uniform(wave_max_u32(pc));
-  load_row<KW>(rs, st, row_chunks(iters), true, row);
-  mask_row<KW>(row, pc);
-  if (!valid) bm = make_uint4(0u, 0u, 0u, 0u);
-  return false;
-}
-
-template <int G, int KMAX>
+// NK > 0: both caches keep exactly NK values per row (straight-line walks);
+// NK == 0: any keep up to KMAX.
+template <int G, int KMAX, int NK>
 __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecodeArgs a) {
   using C = SparseCfg<G>;
-  constexpr int KW = RowCfg<KMAX>::kW;
+  constexpr int NMAX = NK > 0 ? NK : KMAX;
+  constexpr int KW = RowCfg<NMAX>::kW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -295,21 +148,25 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
     float sc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = 0.f;
-    auto score = [&](uint32_t ch, uint32_t vbits) {
+    auto score = [&](uint32_t addr, uint32_t vbits) {
       uint32_t qh[G];
-      load_q<G>(q_lds, ch, qh);
+      load_q<G>(smem + addr, qh);
       const float v = half_bits_to_float(vbits);
 #pragma unroll
       for (int g = 0; g < G; ++g) sc[g] = fmaf(v, half_bits_to_float(qh[g]), sc[g]);
     };
     int kit;
-    if (prepare_rows<KW>(krs, kt0, kk, valid, partial, kb, krow, kit))
-      walk_fast<KMAX, KW>(krow, kb, kit, score);
-    else
-      walk_general<KMAX, KW>(krow, kb, kit, score);
+    if (prepare_rows<KW>(krs, kt0, kk, valid, partial, kb, krow, kit)) {
+      if constexpr (NK > 0)
+        walk_fast<NK, true, C::kQMul>(krow, kb, NK, 0u, score);
+      else
+        walk_fast<KMAX, false, C::kQMul>(krow, kb, kit, 0u, score);
+    } else {
+      walk_general<NMAX, C::kQMul>(krow, kb, kit, 0u, score);
+    }
     if (more) issue_k(tile + 1, kt0n);
 
-    // ---- online softmax in log2 units
+    // ---- online softmax in log2 units; p as fp16 pairs for the dot2 P.V
     float p[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -328,35 +185,45 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
 #pragma unroll
     for (int j = 0; j < (kHeadDim * kTRowBytes) / (16 * kWave); ++j)
       *reinterpret_cast<uint4*>(vt_lds + 16 * (lane + kWave * j)) = make_uint4(0u, 0u, 0u, 0u);
-    uint16_t* p16 = reinterpret_cast<uint16_t*>(p2_lds);
+    {
+      uint16_t* p16 = reinterpret_cast<uint16_t*>(p2_lds);
+      const uint32_t pair = lane >> 1;
+      const uint32_t slot = (pair >> 2) * C::kP2Block + (pair & 3u) * G;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-      p16[((lane >> 1) * G + g) * 2 + (lane & 1)] = float_to_half_bits(p[g]);
+      for (int g = 0; g < G; ++g) p16[(slot + g) * 2 + (lane & 1u)] = float_to_half_bits(p[g]);
+    }
     wave_lds_sync();  // zeros in place before any lane writes its entries
-    char* col = vt_lds + 2 * lane;
-    auto scatter = [&](uint32_t ch, uint32_t vbits) {
-      *reinterpret_cast<uint16_t*>(col + ch * kTRowBytes) = (uint16_t)vbits;
+    auto scatter = [&](uint32_t addr, uint32_t vbits) {
+      *reinterpret_cast<uint16_t*>(smem + addr) = (uint16_t)vbits;
     };
+    const uint32_t col = (uint32_t)(vt_lds - smem) + 2u * lane;
     int vit;
-    if (prepare_rows<KW>(vrs, vt0, vk, valid, partial, vb, vrow, vit))
-      walk_fast<KMAX, KW>(vrow, vb, vit, scatter);
-    else
-      walk_general<KMAX, KW>(vrow, vb, vit, scatter);
+    if (prepare_rows<KW>(vrs, vt0, vk, valid, partial, vb, vrow, vit)) {
+      if constexpr (NK > 0)
+        walk_fast<NK, true, kTRowBytes>(vrow, vb, NK, col, scatter);
+      else
+        walk_fast<KMAX, false, kTRowBytes>(vrow, vb, vit, col, scatter);
+    } else {
+      walk_general<NMAX, kTRowBytes>(vrow, vb, vit, col, scatter);
+    }
     if (more) issue_v(tile + 1, vt0n);
     wave_lds_sync();  // every lane's entries written before the channel-major reads
 
-    // ---- P.V: lane owns channels lane and lane+64; 32 row pairs per tile
-    const char* r0p = vt_lds + lane * kTRowBytes;
-    const char* r1p = vt_lds + (lane + 64) * kTRowBytes;
+    // ---- P.V: lane owns channels lane and lane+64; 32 row pairs per tile, in
+    // 8 blocks of 4 pairs visited in a lane-rotated order (conflict-free reads)
+    const char* r0p = vt_lds + (lane << kTRowShift);
+    const char* r1p = vt_lds + ((lane + 64) << kTRowShift);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint4 x0 = *reinterpret_cast<const uint4*>(r0p + 16 * j);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(r1p + 16 * j);
+      const uint32_t jr = (j + lane) & 7u;
+      const uint4 x0 = *reinterpret_cast<const uint4*>(r0p + 16 * jr);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(r1p + 16 * jr);
       const uint32_t w0[4] = {x0.x, x0.y, x0.z, x0.w};
       const uint32_t w1[4] = {x1.x, x1.y, x1.z, x1.w};
+      const uint32_t* pb = p2_lds + jr * C::kP2Block;
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
-        const uint32_t* pr = p2_lds + (4 * j + pp) * G;
+        const uint32_t* pr = pb + pp * G;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const half2v pv = __builtin_bit_cast(half2v, pr[g]);
@@ -388,32 +255,36 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
   store_split_partial<G>(lds_m, lds_l, lds_acc, G * kHeadDim, kHeadDim, unit, a.splits, s, a.part);
 }
 
-template <int G, int KMAX>
+template <int G, int KMAX, int NK>
 hipError_t launch_sparse_t(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
   constexpr int lds = SparseCfg<G>::kLdsBytes;
   if constexpr (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_sparse_kernel<G, KMAX>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_sparse_kernel<G, KMAX, NK>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_sparse_kernel<G, KMAX>), dim3(a.splits, a.Hkv, batch),
+  hipLaunchKernelGGL((decode_sparse_kernel<G, KMAX, NK>), dim3(a.splits, a.Hkv, batch),
                      dim3(kDecodeBlock), lds, stream, a);
   return hipGetLastError();
 }
 
+// Straight-line kernels for the keeps of 70% and 50% sparsity at head_dim 128
+// (38 and 64); bucketed kernels for any other keep.
 template <int G>
 hipError_t launch_sparse_g(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
+  if (a.kk == a.vk && a.kk == 38) return launch_sparse_t<G, 40, 38>(a, batch, stream);
+  if (a.kk == a.vk && a.kk == 64) return launch_sparse_t<G, 64, 64>(a, batch, stream);
   const int kmax = a.kk > a.vk ? a.kk : a.vk;
-  if (kmax <= 32) return launch_sparse_t<G, 32>(a, batch, stream);
-  if (kmax <= 40) return launch_sparse_t<G, 40>(a, batch, stream);
-  if (kmax <= 48) return launch_sparse_t<G, 48>(a, batch, stream);
-  if (kmax <= 64) return launch_sparse_t<G, 64>(a, batch, stream);
-  return launch_sparse_t<G, 128>(a, batch, stream);
+  if (kmax <= 32) return launch_sparse_t<G, 32, 0>(a, batch, stream);
+  if (kmax <= 48) return launch_sparse_t<G, 48, 0>(a, batch, stream);
+  if (kmax <= 64) return launch_sparse_t<G, 64, 0>(a, batch, stream);
+  return launch_sparse_t<G, 128, 0>(a, batch, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode_sparse(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
+hipError_t launch_decode_sparse_valu(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
   switch (a.Hq / a.Hkv) {
     case 1: return launch_sparse_g<1>(a, batch, stream);
     case 2: return launch_sparse_g<2>(a, batch, stream);

@@ -1,0 +1,310 @@
+// Decode-step attention computed directly over the bitmap-compressed key and
+// value caches ([Summary] "Approach": a custom attention kernel over the bitmap
+// format; [Abstract]; [README] "Part III": batched sparse attention kernel).
+// This is mustafar_decode_attn: the stored entries of each 64-row tile are
+// decoded into LDS and the two contractions over the decoded tile run on the
+// matrix cores.
+//
+// Grid (splits, Hkv, B); 4 waves per block; tiles of a (batch, kv head) are
+// divided among the splits * 4 waves; the block merges its waves into one
+// partial per split and decode_reduce_kernel merges the splits.
+//
+// Per tile, lane t of a wave owns row t of both caches (bitmaps and kept
+// entries in registers, loaded one tile ahead):
+//   key tile    walk the key bitmap and write each kept entry into a zeroed
+//               row-major fp16 tile K[t][c] in LDS (row stride 272 B).
+//   scores      v_mfma_f32_16x16x32_f16: A = 16 tile rows x 32 channels read
+//               from LDS, B = the G query heads as columns (registers), 4 row
+//               blocks x 4 channel blocks; lane l ends with head l%16 of rows
+//               16*mb + 4*(l/16) + i.
+//   softmax     per head: max over the lane's 16 rows and across the 4 lane
+//               groups, exp2, running sums; p to LDS as fp16 p[head][row].
+//   value tile  walk the value bitmap into a zeroed channel-major tile
+//               V[c][t] in the same LDS buffer (row stride 144 B).
+//   P.V         v_mfma_f32_16x16x32_f16: A = 16 channels x 32 rows of V,
+//               B = p[rows][heads]; accumulators out[channel][head] stay in
+//               registers for the whole split (8 channel blocks x 2 row blocks).
+// The strides make every MFMA operand read an optimal 8-cycle ds_read_b128.
+#include "decode_walk.hpp"
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "merge.hpp"
+
+namespace mustafar {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kKRow = 272;  // key tile row: 128 fp16 + 16 B (dump slot, bank spread)
+constexpr uint32_t kVRow = 144;  // value tile channel row: 64 fp16 + 16 B
+constexpr int kTileBytes = 129 * 144;  // value tile + dump row; the key tile (64 x 272) fits too
+
+template <int G>
+struct MfmaCfg {
+  static constexpr int kPBytes = (G + 1) * 128;  // p[head][64] fp16; head row G stays zero
+  static constexpr int kWaveBytes = (kTileBytes + kPBytes + 15) / 16 * 16;
+  static constexpr int kMergeBytes = kDecodeWaves * G * (2 + kHeadDim) * 4;
+  static constexpr int kLdsBytes =
+      kDecodeWaves * kWaveBytes > kMergeBytes ? kDecodeWaves * kWaveBytes : kMergeBytes;
+};
+
+template <int G, int KMAX, int NK>
+__global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
+  using C = MfmaCfg<G>;
+  constexpr int NMAX = NK > 0 ? NK : KMAX;
+  constexpr int KW = RowCfg<NMAX>::kW;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int unit = b * a.Hkv + h;
+  const int wave = wave_uniform((int)(threadIdx.x / kWave));
+  const uint32_t lane = lane_id();
+  const uint32_t l16 = lane & 15u, grp = lane >> 4;
+  int T = a.seq_lens[b];
+  T = T < 0 ? 0 : (T > a.cap ? a.cap : T);
+  const int ntiles = (T + kTile - 1) / kTile;
+  const int ntoff = a.cap / kTile + 1;
+
+  char* tile_lds = smem + wave * C::kWaveBytes;
+  uint16_t* p_lds = reinterpret_cast<uint16_t*>(tile_lds + kTileBytes);  // [G + 1][64]
+  if (lane < 8u) *reinterpret_cast<uint4*>(p_lds + G * 64 + 8 * lane) = make_uint4(0u, 0u, 0u, 0u);
+
+  // B operand of the score MFMA: query heads as columns (zero beyond G)
+  half8 bq[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if ((int)l16 < G)
+      x = *reinterpret_cast<const uint4*>(
+          a.q + ((int64_t)b * a.Hq + h * G + l16) * kHeadDim + 32 * kb + 8 * grp);
+    bq[kb] = __builtin_bit_cast(half8, x);
+  }
+
+  const float ninf = -__builtin_inff();
+  float m = ninf, lsum = 0.f;  // head l16
+  floatx4 acc[8];              // out[channel 16*mb + 4*grp + i][head l16]
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int total_waves = a.splits * kDecodeWaves;
+  const int wid = s * kDecodeWaves + wave;
+  const int tpw = (ntiles + total_waves - 1) / total_waves;
+  const int tb = min(wid * tpw, ntiles), te = min(tb + tpw, ntiles);
+
+  const int kk = a.kk, vk = a.vk;
+  const auto krs = make_rsrc(a.kval + (int64_t)unit * a.cap * kk, (uint32_t)a.cap * kk * 2u);
+  const auto vrs = make_rsrc(a.vval + (int64_t)unit * a.cap * vk, (uint32_t)a.cap * vk * 2u);
+  const auto kbrs = make_rsrc(a.kbm + (int64_t)unit * a.cap * 2, (uint32_t)a.cap * 16u);
+  const auto vbrs = make_rsrc(a.vbm + (int64_t)unit * a.cap * 2, (uint32_t)a.cap * 16u);
+  const auto ktrs = make_rsrc(a.ktoff + (int64_t)unit * ntoff, (uint32_t)ntoff * 4u);
+  const auto vtrs = make_rsrc(a.vtoff + (int64_t)unit * ntoff, (uint32_t)ntoff * 4u);
+  const int kch = row_chunks(kk), vch = row_chunks(vk);
+  const bool k_odd = (kk & 1) != 0, v_odd = (vk & 1) != 0;
+
+  // tile offsets of this wave's tiles, 64 at a time, one per lane
+  int toff_base = tb;
+  uint32_t ktv = buf_load4(ktrs, (uint32_t)(tb + lane) * 4u);
+  uint32_t vtv = buf_load4(vtrs, (uint32_t)(tb + lane) * 4u);
+  auto offsets = [&](int tile, uint32_t& kt0, uint32_t& vt0) {
+    if (tile - toff_base >= kWave) {
+      toff_base = tile;
+      ktv = buf_load4(ktrs, (uint32_t)(tile + lane) * 4u);
+      vtv = buf_load4(vtrs, (uint32_t)(tile + lane) * 4u);
+    }
+    kt0 = __builtin_amdgcn_readlane(ktv, tile - toff_base);
+    vt0 = __builtin_amdgcn_readlane(vtv, tile - toff_base);
+  };
+
+  uint4 kb, vb;
+  uint32_t krow[KW], vrow[KW];
+  uint32_t kt0 = 0, vt0 = 0, kt0n = 0, vt0n = 0;
+  auto issue_k = [&](int tile, uint32_t t0) {
+    kb = buf_load16(kbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
+    load_row<KW>(krs, t0 + lane * (uint32_t)kk, kch, k_odd || (t0 & 1u), krow);
+  };
+  auto issue_v = [&](int tile, uint32_t t0) {
+    vb = buf_load16(vbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
+    load_row<KW>(vrs, t0 + lane * (uint32_t)vk, vch, v_odd || (t0 & 1u), vrow);
+  };
+  if (tb < te) {
+    offsets(tb, kt0, vt0);
+    issue_k(tb, kt0);
+    issue_v(tb, vt0);
+  }
+  auto scatter = [&](uint32_t addr, uint32_t vbits) {
+    *reinterpret_cast<uint16_t*>(tile_lds + addr) = (uint16_t)vbits;
+  };
+
+  for (int tile = tb; tile < te; ++tile) {
+    const int nvalid = min(kTile, T - tile * kTile);
+    const bool valid = (int)lane < nvalid;
+    const bool partial = nvalid < kTile;
+    const bool more = tile + 1 < te;
+    if (more) offsets(tile + 1, kt0n, vt0n);
+
+    // ---- key tile K[t][c]
+    wave_lds_sync();  // the previous tile's reads of the buffer are done
+#pragma unroll
+    for (int j = 0; j < (64 * (int)kKRow) / (16 * kWave); ++j)
+      *reinterpret_cast<uint4*>(tile_lds + 16 * (lane + kWave * j)) = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_sync();
+    int kit;
+    if (prepare_rows<KW>(krs, kt0, kk, valid, partial, kb, krow, kit)) {
+      if constexpr (NK > 0)
+        walk_fast<NK, true, 2u>(krow, kb, NK, lane * kKRow, scatter);
+      else
+        walk_fast<KMAX, false, 2u>(krow, kb, kit, lane * kKRow, scatter);
+    } else {
+      walk_general<NMAX, 2u>(krow, kb, kit, lane * kKRow, scatter);
+    }
+    if (more) issue_k(tile + 1, kt0n);
+    wave_lds_sync();
+
+    // ---- scores: 4 row blocks x 4 channel blocks
+    floatx4 cs[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      cs[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const char* rowp = tile_lds + (16 * mb + l16) * kKRow + 16 * grp;
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(rowp + 64 * kb4);
+        cs[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, x), bq[kb4],
+                                                        cs[mb], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax for head l16 (log2 units)
+    float sv[16];
+    float mt = ninf;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mb + 4 * (int)grp + i;
+        sv[4 * mb + i] = (r < nvalid) ? cs[mb][i] * a.scale_log2 : ninf;
+        mt = fmaxf(mt, sv[4 * mb + i]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    const float mn = fmaxf(m, mt);
+    const float alpha = exp2f(m - mn);
+    m = mn;
+    float ps = 0.f;
+    uint32_t ph[8];  // fp16 pairs for p_lds
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const float p0 = exp2f(sv[4 * mb + 0] - mn), p1 = exp2f(sv[4 * mb + 1] - mn);
+      const float p2 = exp2f(sv[4 * mb + 2] - mn), p3 = exp2f(sv[4 * mb + 3] - mn);
+      ps += (p0 + p1) + (p2 + p3);
+      ph[2 * mb] = (uint32_t)float_to_half_bits(p0) | ((uint32_t)float_to_half_bits(p1) << 16);
+      ph[2 * mb + 1] = (uint32_t)float_to_half_bits(p2) | ((uint32_t)float_to_half_bits(p3) << 16);
+    }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
+    if ((int)l16 < G) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        *reinterpret_cast<uint2*>(p_lds + l16 * 64 + 16 * mb + 4 * grp) =
+            make_uint2(ph[2 * mb], ph[2 * mb + 1]);
+    }
+
+    // ---- value tile V[c][t] in the same buffer
+    wave_lds_sync();  // score reads of the key tile done; p written
+#pragma unroll
+    for (int j = 0; j < (kHeadDim * (int)kVRow) / (16 * kWave); ++j)
+      *reinterpret_cast<uint4*>(tile_lds + 16 * (lane + kWave * j)) = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_sync();
+    int vit;
+    if (prepare_rows<KW>(vrs, vt0, vk, valid, partial, vb, vrow, vit)) {
+      if constexpr (NK > 0)
+        walk_fast<NK, true, kVRow>(vrow, vb, NK, 2u * lane, scatter);
+      else
+        walk_fast<KMAX, false, kVRow>(vrow, vb, vit, 2u * lane, scatter);
+    } else {
+      walk_general<NMAX, kVRow>(vrow, vb, vit, 2u * lane, scatter);
+    }
+    if (more) issue_v(tile + 1, vt0n);
+    wave_lds_sync();
+
+    // ---- P.V: 8 channel blocks x 2 row blocks
+    const uint16_t* prow = p_lds + (l16 < (uint32_t)G ? l16 : (uint32_t)G) * 64 + 8 * grp;
+    const half8 pb0 = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(prow));
+    const half8 pb1 = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(prow + 32));
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const char* vrowp = tile_lds + (16 * mb + l16) * kVRow + 16 * grp;
+      const uint4 x0 = *reinterpret_cast<const uint4*>(vrowp);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(vrowp + 64);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, x0), pb0, acc[mb],
+                                                       0, 0, 0);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, x1), pb1, acc[mb],
+                                                       0, 0, 0);
+    }
+    kt0 = kt0n;
+    vt0 = vt0n;
+  }
+
+  lsum += __shfl_xor(lsum, 16, kWave);
+  lsum += __shfl_xor(lsum, 32, kWave);
+  __syncthreads();  // the merge area overlaps the per-wave buffers
+  float* lds_m = reinterpret_cast<float*>(smem);
+  float* lds_l = lds_m + kDecodeWaves * G;
+  float* lds_acc = lds_l + kDecodeWaves * G;
+  if ((int)l16 < G) {
+    if (grp == 0u) {
+      lds_m[wave * G + l16] = m;
+      lds_l[wave * G + l16] = lsum;
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lds_acc[(wave * G + l16) * kHeadDim + 16 * mb + 4 * grp + i] = acc[mb][i];
+  }
+  __syncthreads();
+  store_split_partial<G>(lds_m, lds_l, lds_acc, G * kHeadDim, kHeadDim, unit, a.splits, s, a.part);
+}
+
+template <int G, int KMAX, int NK>
+hipError_t launch_mfma_t(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
+  constexpr int lds = MfmaCfg<G>::kLdsBytes;
+  if constexpr (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_sparse_mfma_kernel<G, KMAX, NK>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_sparse_mfma_kernel<G, KMAX, NK>), dim3(a.splits, a.Hkv, batch),
+                     dim3(kDecodeBlock), lds, stream, a);
+  return hipGetLastError();
+}
+
+// Straight-line walks for the keeps of 70% and 50% sparsity at head_dim 128
+// (38 and 64); bucketed walks for any other keep.
+template <int G>
+hipError_t launch_mfma_g(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
+  if (a.kk == a.vk && a.kk == 38) return launch_mfma_t<G, 40, 38>(a, batch, stream);
+  if (a.kk == a.vk && a.kk == 64) return launch_mfma_t<G, 64, 64>(a, batch, stream);
+  const int kmax = a.kk > a.vk ? a.kk : a.vk;
+  if (kmax <= 32) return launch_mfma_t<G, 32, 0>(a, batch, stream);
+  if (kmax <= 48) return launch_mfma_t<G, 48, 0>(a, batch, stream);
+  if (kmax <= 64) return launch_mfma_t<G, 64, 0>(a, batch, stream);
+  return launch_mfma_t<G, 128, 0>(a, batch, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode_sparse(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_mfma_g<1>(a, batch, stream);
+    case 2: return launch_mfma_g<2>(a, batch, stream);
+    case 4: return launch_mfma_g<4>(a, batch, stream);
+    case 8: return launch_mfma_g<8>(a, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mustafar

@@ -1,0 +1,176 @@
+// Shared pieces of the sparse decode kernels: loading a tile's rows into
+// registers and walking a row's bitmap set bit by set bit.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace mustafar {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+template <int KMAX>
+struct RowCfg {
+  static constexpr int kChunks = (KMAX / 2 + 1 + 3) / 4;  // 16 B chunks per row (+1 dword for realign)
+  static constexpr int kW = kChunks * 4;                   // dwords of a row in registers
+};
+
+// q[c][g] for the G heads of the group, from the LDS table q[c][g] at byte
+// address `addr` = table + c * 2G.
+template <int G>
+__device__ __forceinline__ void load_q(const char* addr, uint32_t (&qh)[G]) {
+  if constexpr (G == 1) {
+    qh[0] = *reinterpret_cast<const uint16_t*>(addr);
+  } else if constexpr (G == 2) {
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(addr);
+    qh[0] = x & 0xFFFFu;
+    qh[1] = x >> 16;
+  } else if constexpr (G == 4) {
+    const uint2 x = *reinterpret_cast<const uint2*>(addr);
+    qh[0] = x.x & 0xFFFFu; qh[1] = x.x >> 16; qh[2] = x.y & 0xFFFFu; qh[3] = x.y >> 16;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(addr);
+    qh[0] = x.x & 0xFFFFu; qh[1] = x.x >> 16; qh[2] = x.y & 0xFFFFu; qh[3] = x.y >> 16;
+    qh[4] = x.z & 0xFFFFu; qh[5] = x.z >> 16; qh[6] = x.w & 0xFFFFu; qh[7] = x.w >> 16;
+  }
+}
+
+template <int KW>
+__device__ __forceinline__ uint32_t value_at(const uint32_t (&row)[KW], int i) {
+  const uint32_t w = row[i >> 1];
+  return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// Walks over the set bits of a row.  For the n-th set bit (channel c) the
+// callback gets f(base + c * MUL, stored value n): callers pass the address of
+// channel 0 in their own table as `base` and the byte stride of a channel as
+// MUL (a shift or one v_mad_u32_u24).
+//
+// Fast walk: every valid row holds exactly n set bits and all four bitmap
+// dwords are non-zero (invalid lanes carry all-ones words and zero values), so
+// the next dword is never empty and no lane runs out before the last step.
+// With EXACT the count is the compile-time NMAX and the walk is straight-line
+// code the compiler can software-pipeline.
+template <int NMAX, bool EXACT, uint32_t MUL, int KW, class F>
+__device__ __forceinline__ void walk_fast(const uint32_t (&row)[KW], uint4 w, int n, uint32_t base,
+                                          F&& f) {
+  uint32_t cur = w.x, n1 = w.y, n2 = w.z, n3 = w.w;
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) {
+    if (EXACT || i < n) {
+      f(base + (uint32_t)__builtin_ctz(cur) * MUL, value_at(row, i));
+      cur &= cur - 1u;
+      const bool z = (cur == 0u);
+      cur = z ? n1 : cur;
+      n1 = z ? n2 : n1;
+      n2 = z ? n3 : n2;
+      base += z ? 32u * MUL : 0u;
+    }
+  }
+}
+
+// General walk: empty dwords are compacted away (each kept dword carries its
+// channel base) and a lane that has used all its set bits reports channel 128
+// (the zero q entry / the dump row); its remaining values are zero.
+template <int NMAX, uint32_t MUL, int KW, class F>
+__device__ __forceinline__ void walk_general(const uint32_t (&row)[KW], uint4 w, int iters,
+                                             uint32_t base, F&& f) {
+  const uint32_t dump = base + 128u * MUL;
+  uint32_t cw[4] = {w.x, w.y, w.z, w.w};
+  uint32_t cb[4] = {base, base + 32u * MUL, base + 64u * MUL, base + 96u * MUL};
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const bool sw = (cw[j] == 0u) && (cw[j + 1] != 0u);
+      const uint32_t a = cw[j], ab = cb[j];
+      cw[j] = sw ? cw[j + 1] : cw[j];
+      cb[j] = sw ? cb[j + 1] : cb[j];
+      cw[j + 1] = sw ? a : cw[j + 1];
+      cb[j + 1] = sw ? ab : cb[j + 1];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cb[j] = cw[j] ? cb[j] : dump;
+  uint32_t cur = cw[0], b0 = cb[0], n1 = cw[1], b1 = cb[1], n2 = cw[2], b2 = cb[2], n3 = cw[3],
+           b3 = cb[3];
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) {
+    if (i < iters) {
+      f(cur ? b0 + (uint32_t)__builtin_ctz(cur) * MUL : dump, value_at(row, i));
+      cur &= cur - 1u;
+      const bool z = (cur == 0u);
+      cur = z ? n1 : cur; b0 = z ? b1 : b0;
+      n1 = z ? n2 : n1; b1 = z ? b2 : b1;
+      n2 = z ? n3 : n2; b2 = z ? b3 : b2;
+      n3 = z ? 0u : n3; b3 = z ? dump : b3;
+    }
+  }
+}
+
+// Loads dwords of the stored values from half index `start` of the region
+// and shifts them so that row[i] holds values 2i and 2i+1 of the row.
+template <int KW>
+__device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, uint32_t start, int nchunks,
+                                         bool odd_possible, uint32_t (&row)[KW]) {
+  const uint32_t dw0 = start >> 1;
+#pragma unroll
+  for (int j = 0; j < KW / 4; ++j) {
+    uint4 c = make_uint4(0u, 0u, 0u, 0u);
+    if (j < nchunks) c = buf_load16(rs, (dw0 + 4u * j) * 4u);
+    row[4 * j + 0] = c.x; row[4 * j + 1] = c.y; row[4 * j + 2] = c.z; row[4 * j + 3] = c.w;
+  }
+  if (odd_possible) {
+    const bool odd = start & 1u;
+#pragma unroll
+    for (int j = 0; j < KW - 1; ++j)
+      row[j] = odd ? __builtin_amdgcn_alignbit(row[j + 1], row[j], 16u) : row[j];
+  }
+}
+
+// Chunks of 16 B covering n values starting at any half offset (+1 dword slack).
+__device__ __forceinline__ int row_chunks(int n) { return (((n + 1) >> 1) + 1 + 3) >> 2; }
+
+// Zeroes stored values beyond the first `count` of the row.
+template <int KW>
+__device__ __forceinline__ void mask_row(uint32_t (&row)[KW], uint32_t count) {
+#pragma unroll
+  for (int j = 0; j < KW; ++j) {
+    const uint32_t lo_ok = (2u * j < count) ? 0xFFFFu : 0u;
+    const uint32_t hi_ok = (2u * j + 1u < count) ? 0xFFFF0000u : 0u;
+    row[j] &= (lo_ok | hi_ok);
+  }
+}
+
+__device__ __forceinline__ uint32_t pop4(uint4 w) {
+  return __popc(w.x) + __popc(w.y) + __popc(w.z) + __popc(w.w);
+}
+
+// Prepares one side's rows for a walk and reports whether the fast walk applies
+// to the whole wave.  Rows were loaded at the start each would have if every row
+// held exactly `keep` values; when that does not hold the rows are reloaded from
+// their exact starts (prefix sum of the popcounts).
+template <int KW>
+__device__ __forceinline__ bool prepare_rows(__amdgpu_buffer_rsrc_t rs, uint32_t toff, int keep,
+                                             bool valid, bool partial, uint4& bm,
+                                             uint32_t (&row)[KW], int& iters) {
+  const uint32_t pop = pop4(bm);
+  const bool lane_fast = !valid || (pop == (uint32_t)keep && bm.x && bm.y && bm.z && bm.w);
+  if (__ballot(!lane_fast) == 0ull) {
+    if (partial) {
+      if (!valid) bm = make_uint4(~0u, ~0u, ~0u, ~0u);
+#pragma unroll
+      for (int j = 0; j < KW; ++j) row[j] = valid ? row[j] : 0u;
+    }
+    iters = keep;
+    return true;
+  }
+  const uint32_t pc = valid ? pop : 0u;
+  const uint32_t st = toff + wave_excl_scan(pc);
+  iters = (int)wave_uniform(wave_max_u32(pc));
+  load_row<KW>(rs, st, row_chunks(iters), true, row);
+  mask_row<KW>(row, pc);
+  if (!valid) bm = make_uint4(0u, 0u, 0u, 0u);
+  return false;
+}
+
+}  // namespace mustafar

@@ -48,6 +48,7 @@ hipError_t launch_append(const mustafar_kv_t& k, const mustafar_kv_t& v, const u
                          const uint16_t* v_new, int32_t* seq_lens, uint32_t* status,
                          hipStream_t stream);
 hipError_t launch_decode_sparse(const SparseDecodeArgs& a, int batch, hipStream_t stream);
+hipError_t launch_decode_sparse_valu(const SparseDecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_decode_dense(const DenseDecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_decode_reduce(const float* part, int batch, int hq, int hkv, int splits,
                                 uint16_t* out, hipStream_t stream);
