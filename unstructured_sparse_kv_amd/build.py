@@ -19,11 +19,17 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# Matrix-core kernels: MFMA accumulators in ordinary VGPRs, so the vector code
+# that rescales them needs no copies to and from the accumulation registers.
+FILE_FLAGS = {
+    "decode_sparse_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ["hipcc", *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

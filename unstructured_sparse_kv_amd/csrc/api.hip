@@ -53,7 +53,7 @@ int launched(hipError_t e) { return e == hipSuccess ? MUSTAFAR_OK : MUSTAFAR_ELA
 int auto_splits(int64_t batch, int64_t hkv, int64_t max_seq_len) {
   const int64_t units = batch * hkv;
   const int64_t tiles = (max_seq_len + 63) / 64;
-  const int64_t target_blocks = 1024;  // about four 4-wave blocks per compute unit
+  const int64_t target_blocks = 512;  // two 4-wave blocks per compute unit (LDS-bound occupancy)
   int64_t s = (target_blocks + units - 1) / units;
   const int64_t most = (tiles + 2 * kDecodeWaves - 1) / (2 * kDecodeWaves);  // >= 2 tiles per wave
   if (s > most) s = most;

@@ -120,16 +120,17 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
   // One register set per side, refilled for the next tile as soon as the
   // current tile's walk over it is done (keys after the key walk, values after
   // the value walk), so each side's loads overlap the rest of the tile.
+  constexpr bool kEvenExact = NK > 0 && NK % 2 == 0;  // see the matrix-core kernel
   uint4 kb, vb;
   uint32_t krow[KW], vrow[KW];
   uint32_t kt0 = 0, vt0 = 0, kt0n = 0, vt0n = 0;
   auto issue_k = [&](int tile, uint32_t t0) {
     kb = buf_load16(kbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
-    load_row<KW>(krs, t0 + lane * (uint32_t)kk, kch, k_odd || (t0 & 1u), krow);
+    load_row<KW>(krs, t0 + lane * (uint32_t)kk, kch, !kEvenExact && (k_odd || (t0 & 1u)), krow);
   };
   auto issue_v = [&](int tile, uint32_t t0) {
     vb = buf_load16(vbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
-    load_row<KW>(vrs, t0 + lane * (uint32_t)vk, vch, v_odd || (t0 & 1u), vrow);
+    load_row<KW>(vrs, t0 + lane * (uint32_t)vk, vch, !kEvenExact && (v_odd || (t0 & 1u)), vrow);
   };
   if (tb < te) {
     offsets(tb, kt0, vt0);
@@ -141,8 +142,8 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
     const int nvalid = min(kTile, T - tile * kTile);
     const bool valid = (int)lane < nvalid;
     const bool partial = nvalid < kTile;
-    const bool more = tile + 1 < te;
-    if (more) offsets(tile + 1, kt0n, vt0n);
+    const int nxt = min(tile + 1, te - 1);  // the last tile reloads itself
+    offsets(nxt, kt0n, vt0n);
 
     // ---- key side: scores for the G heads
     float sc[G];
@@ -155,16 +156,10 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
 #pragma unroll
       for (int g = 0; g < G; ++g) sc[g] = fmaf(v, half_bits_to_float(qh[g]), sc[g]);
     };
-    int kit;
-    if (prepare_rows<KW>(krs, kt0, kk, valid, partial, kb, krow, kit)) {
-      if constexpr (NK > 0)
-        walk_fast<NK, true, C::kQMul>(krow, kb, NK, 0u, score);
-      else
-        walk_fast<KMAX, false, C::kQMul>(krow, kb, kit, 0u, score);
-    } else {
-      walk_general<NMAX, C::kQMul>(krow, kb, kit, 0u, score);
-    }
-    if (more) issue_k(tile + 1, kt0n);
+    // lanes past the end read q entries like the others; their scores are masked
+    decode_side<NMAX, NK, true, C::kQMul>(krs, kt0, kk, valid, partial, !kEvenExact || !(kt0 & 1u),
+                                          kb, krow, 0u, 0u, score);
+    issue_k(nxt, kt0n);
 
     // ---- online softmax in log2 units; p as fp16 pairs for the dot2 P.V
     float p[G];
@@ -172,8 +167,8 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
     for (int g = 0; g < G; ++g) {
       const float sv = valid ? sc[g] * a.scale_log2 : ninf;
       const float mn = fmaxf(m[g], wave_max(sv));
-      const float alpha = exp2f(m[g] - mn);
-      p[g] = exp2f(sv - mn);
+      const float alpha = exp2_raw(m[g] - mn);
+      p[g] = exp2_raw(sv - mn);
       lsum[g] = lsum[g] * alpha + p[g];
       acc0[g] *= alpha;
       acc1[g] *= alpha;
@@ -197,16 +192,9 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
       *reinterpret_cast<uint16_t*>(smem + addr) = (uint16_t)vbits;
     };
     const uint32_t col = (uint32_t)(vt_lds - smem) + 2u * lane;
-    int vit;
-    if (prepare_rows<KW>(vrs, vt0, vk, valid, partial, vb, vrow, vit)) {
-      if constexpr (NK > 0)
-        walk_fast<NK, true, kTRowBytes>(vrow, vb, NK, col, scatter);
-      else
-        walk_fast<KMAX, false, kTRowBytes>(vrow, vb, vit, col, scatter);
-    } else {
-      walk_general<NMAX, kTRowBytes>(vrow, vb, vit, col, scatter);
-    }
-    if (more) issue_v(tile + 1, vt0n);
+    decode_side<NMAX, NK, false, kTRowBytes>(vrs, vt0, vk, valid, partial,
+                                             !kEvenExact || !(vt0 & 1u), vb, vrow, col, 0u, scatter);
+    issue_v(nxt, vt0n);
     wave_lds_sync();  // every lane's entries written before the channel-major reads
 
     // ---- P.V: lane owns channels lane and lane+64; 32 row pairs per tile, in

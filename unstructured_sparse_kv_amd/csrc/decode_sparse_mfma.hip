@@ -18,7 +18,10 @@
 //               blocks x 4 channel blocks; lane l ends with head l%16 of rows
 //               16*mb + 4*(l/16) + i.
 //   softmax     per head: max over the lane's 16 rows and across the 4 lane
-//               groups, exp2, running sums; p to LDS as fp16 p[head][row].
+//               groups; the running reference max is raised (and the
+//               accumulators rescaled) only when a score exceeds it by more
+//               than 8 in log2 units, so p <= 2^8; exp2, running sums; p to
+//               LDS as fp16 p[head][row].
 //   value tile  walk the value bitmap into a zeroed channel-major tile
 //               V[c][t] in the same LDS buffer (row stride 144 B).
 //   P.V         v_mfma_f32_16x16x32_f16: A = 16 channels x 32 rows of V,
@@ -39,6 +42,13 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kKRow = 272;  // key tile row: 128 fp16 + 16 B (dump slot, bank spread)
 constexpr uint32_t kVRow = 144;  // value tile channel row: 64 fp16 + 16 B
 constexpr int kTileBytes = 129 * 144;  // value tile + dump row; the key tile (64 x 272) fits too
+// Writes of lanes past the end of the sequence: a key row after the 64 tile
+// rows (free while the key tile is in use) and, for values, the padding
+// column 64 of every channel row.
+constexpr uint32_t kKDump = 64 * kKRow;
+constexpr uint32_t kVDump = 128;
+static_assert(kKDump + kKRow <= (uint32_t)kTileBytes, "key dump row inside the tile buffer");
+constexpr float kRescaleSlack = 8.f;   // log2 units
 
 template <int G>
 struct MfmaCfg {
@@ -116,32 +126,39 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
     vt0 = __builtin_amdgcn_readlane(vtv, tile - toff_base);
   };
 
+  // One register set per side, refilled for the next tile (the last tile
+  // reloads itself, so the loads need no condition) as soon as the current
+  // tile's walk over it is done.  With an even exact keep every row start is
+  // even unless the caches break the format; such a start sends the tile to
+  // the general path, so the fast loads skip the realignment.
+  constexpr bool kEvenExact = NK > 0 && NK % 2 == 0;
   uint4 kb, vb;
   uint32_t krow[KW], vrow[KW];
   uint32_t kt0 = 0, vt0 = 0, kt0n = 0, vt0n = 0;
   auto issue_k = [&](int tile, uint32_t t0) {
     kb = buf_load16(kbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
-    load_row<KW>(krs, t0 + lane * (uint32_t)kk, kch, k_odd || (t0 & 1u), krow);
+    load_row<KW>(krs, t0 + lane * (uint32_t)kk, kch, !kEvenExact && (k_odd || (t0 & 1u)), krow);
   };
   auto issue_v = [&](int tile, uint32_t t0) {
     vb = buf_load16(vbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
-    load_row<KW>(vrs, t0 + lane * (uint32_t)vk, vch, v_odd || (t0 & 1u), vrow);
+    load_row<KW>(vrs, t0 + lane * (uint32_t)vk, vch, !kEvenExact && (v_odd || (t0 & 1u)), vrow);
   };
   if (tb < te) {
     offsets(tb, kt0, vt0);
     issue_k(tb, kt0);
     issue_v(tb, vt0);
   }
+  const uint32_t tile_base = (uint32_t)(tile_lds - smem);
   auto scatter = [&](uint32_t addr, uint32_t vbits) {
-    *reinterpret_cast<uint16_t*>(tile_lds + addr) = (uint16_t)vbits;
+    *reinterpret_cast<uint16_t*>(smem + addr) = (uint16_t)vbits;
   };
 
   for (int tile = tb; tile < te; ++tile) {
     const int nvalid = min(kTile, T - tile * kTile);
     const bool valid = (int)lane < nvalid;
     const bool partial = nvalid < kTile;
-    const bool more = tile + 1 < te;
-    if (more) offsets(tile + 1, kt0n, vt0n);
+    const int nxt = min(tile + 1, te - 1);
+    offsets(nxt, kt0n, vt0n);
 
     // ---- key tile K[t][c]
     wave_lds_sync();  // the previous tile's reads of the buffer are done
@@ -149,16 +166,9 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
     for (int j = 0; j < (64 * (int)kKRow) / (16 * kWave); ++j)
       *reinterpret_cast<uint4*>(tile_lds + 16 * (lane + kWave * j)) = make_uint4(0u, 0u, 0u, 0u);
     wave_lds_sync();
-    int kit;
-    if (prepare_rows<KW>(krs, kt0, kk, valid, partial, kb, krow, kit)) {
-      if constexpr (NK > 0)
-        walk_fast<NK, true, 2u>(krow, kb, NK, lane * kKRow, scatter);
-      else
-        walk_fast<KMAX, false, 2u>(krow, kb, kit, lane * kKRow, scatter);
-    } else {
-      walk_general<NMAX, 2u>(krow, kb, kit, lane * kKRow, scatter);
-    }
-    if (more) issue_k(tile + 1, kt0n);
+    decode_side<NMAX, NK, true, 2u>(krs, kt0, kk, valid, partial, !kEvenExact || !(kt0 & 1u), kb,
+                                    krow, tile_base + lane * kKRow, tile_base + kKDump, scatter);
+    issue_k(nxt, kt0n);
     wave_lds_sync();
 
     // ---- scores: 4 row blocks x 4 channel blocks
@@ -177,33 +187,45 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
 
     // ---- online softmax for head l16 (log2 units)
     float sv[16];
-    float mt = ninf;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mb + 4 * (int)grp + i;
-        sv[4 * mb + i] = (r < nvalid) ? cs[mb][i] * a.scale_log2 : ninf;
-        mt = fmaxf(mt, sv[4 * mb + i]);
-      }
+      for (int i = 0; i < 4; ++i) sv[4 * mb + i] = cs[mb][i] * a.scale_log2;
+    if (partial) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sv[4 * mb + i] = (16 * mb + 4 * (int)grp + i < nvalid) ? sv[4 * mb + i] : ninf;
+    }
+    float mt = ninf;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sv[j]);
     mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float mn = fmaxf(m, mt);
-    const float alpha = exp2f(m - mn);
-    m = mn;
+    // The reference m moves only when a score exceeds it by more than
+    // kRescaleSlack, so p stays below 2^kRescaleSlack (well inside the fp16
+    // range, same relative precision); most tiles skip the rescale.
+    if (__ballot(mt > m + kRescaleSlack) != 0ull) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = exp2_raw(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
+    }
+    const float mn = m;
     float ps = 0.f;
     uint32_t ph[8];  // fp16 pairs for p_lds
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const float p0 = exp2f(sv[4 * mb + 0] - mn), p1 = exp2f(sv[4 * mb + 1] - mn);
-      const float p2 = exp2f(sv[4 * mb + 2] - mn), p3 = exp2f(sv[4 * mb + 3] - mn);
+      const float p0 = exp2_raw(sv[4 * mb + 0] - mn), p1 = exp2_raw(sv[4 * mb + 1] - mn);
+      const float p2 = exp2_raw(sv[4 * mb + 2] - mn), p3 = exp2_raw(sv[4 * mb + 3] - mn);
       ps += (p0 + p1) + (p2 + p3);
       ph[2 * mb] = (uint32_t)float_to_half_bits(p0) | ((uint32_t)float_to_half_bits(p1) << 16);
       ph[2 * mb + 1] = (uint32_t)float_to_half_bits(p2) | ((uint32_t)float_to_half_bits(p3) << 16);
     }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
+    lsum += ps;
     if ((int)l16 < G) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
@@ -217,16 +239,9 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
     for (int j = 0; j < (kHeadDim * (int)kVRow) / (16 * kWave); ++j)
       *reinterpret_cast<uint4*>(tile_lds + 16 * (lane + kWave * j)) = make_uint4(0u, 0u, 0u, 0u);
     wave_lds_sync();
-    int vit;
-    if (prepare_rows<KW>(vrs, vt0, vk, valid, partial, vb, vrow, vit)) {
-      if constexpr (NK > 0)
-        walk_fast<NK, true, kVRow>(vrow, vb, NK, 2u * lane, scatter);
-      else
-        walk_fast<KMAX, false, kVRow>(vrow, vb, vit, 2u * lane, scatter);
-    } else {
-      walk_general<NMAX, kVRow>(vrow, vb, vit, 2u * lane, scatter);
-    }
-    if (more) issue_v(tile + 1, vt0n);
+    decode_side<NMAX, NK, true, kVRow>(vrs, vt0, vk, valid, partial, !kEvenExact || !(vt0 & 1u), vb,
+                                       vrow, tile_base + 2u * lane, tile_base + kVDump, scatter);
+    issue_v(nxt, vt0n);
     wave_lds_sync();
 
     // ---- P.V: 8 channel blocks x 2 row blocks

@@ -130,14 +130,16 @@ __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, uint32_t sta
 // Chunks of 16 B covering n values starting at any half offset (+1 dword slack).
 __device__ __forceinline__ int row_chunks(int n) { return (((n + 1) >> 1) + 1 + 3) >> 2; }
 
-// Zeroes stored values beyond the first `count` of the row.
+// Zeroes stored values beyond the first `count` of the row.  The masks come
+// from sign bits (all ones where the index is below count) rather than from
+// compares, which would each hold a scalar register pair.
 template <int KW>
 __device__ __forceinline__ void mask_row(uint32_t (&row)[KW], uint32_t count) {
 #pragma unroll
   for (int j = 0; j < KW; ++j) {
-    const uint32_t lo_ok = (2u * j < count) ? 0xFFFFu : 0u;
-    const uint32_t hi_ok = (2u * j + 1u < count) ? 0xFFFF0000u : 0u;
-    row[j] &= (lo_ok | hi_ok);
+    const uint32_t lo = (uint32_t)((int32_t)(2u * j - count) >> 31);
+    const uint32_t hi = (uint32_t)((int32_t)(2u * j + 1u - count) >> 31);
+    row[j] &= (lo & 0xFFFFu) | (hi & 0xFFFF0000u);
   }
 }
 
@@ -145,32 +147,56 @@ __device__ __forceinline__ uint32_t pop4(uint4 w) {
   return __popc(w.x) + __popc(w.y) + __popc(w.z) + __popc(w.w);
 }
 
-// Prepares one side's rows for a walk and reports whether the fast walk applies
-// to the whole wave.  Rows were loaded at the start each would have if every row
-// held exactly `keep` values; when that does not hold the rows are reloaded from
-// their exact starts (prefix sum of the popcounts).
-template <int KW>
-__device__ __forceinline__ bool prepare_rows(__amdgpu_buffer_rsrc_t rs, uint32_t toff, int keep,
-                                             bool valid, bool partial, uint4& bm,
-                                             uint32_t (&row)[KW], int& iters) {
+// Decodes one side (keys or values) of a 64-row tile: for every stored entry of
+// the lane's row, f(base + channel * MUL, value bits).
+//
+// The rows were prefetched into `row` from the start each would have if every
+// row held exactly `keep` values (`start_ok`: that load also handled an odd
+// start).  When every valid row of the wave has exactly `keep` set bits spread
+// over all four bitmap dwords, the fast walk runs on the prefetched registers
+// as they are: lanes past the end of the sequence walk an all-ones bitmap and
+// either write to `dump` (REDIRECT: a region that absorbs keep * MUL bytes and
+// is never read) or have their values zeroed.  Otherwise the rows are reloaded
+// from their exact starts (prefix sum of the popcounts) into registers of
+// their own and walked by the general walk; lanes past the end walk nothing.
+// The prefetched registers are only read here, so the next prefetch can
+// overwrite them in place.
+template <int NMAX, int NK, bool REDIRECT, uint32_t MUL, int KW, class F>
+__device__ __forceinline__ void decode_side(__amdgpu_buffer_rsrc_t rs, uint32_t toff, int keep,
+                                            bool valid, bool partial, bool start_ok, uint4 bm,
+                                            const uint32_t (&row)[KW], uint32_t base,
+                                            uint32_t dump, F&& f) {
   const uint32_t pop = pop4(bm);
   const bool lane_fast = !valid || (pop == (uint32_t)keep && bm.x && bm.y && bm.z && bm.w);
-  if (__ballot(!lane_fast) == 0ull) {
-    if (partial) {
-      if (!valid) bm = make_uint4(~0u, ~0u, ~0u, ~0u);
+  if (start_ok && __ballot(!lane_fast) == 0ull) {
+    if (!partial) {
+      if constexpr (NK > 0) walk_fast<NK, true, MUL>(row, bm, NK, base, f);
+      else walk_fast<NMAX, false, MUL>(row, bm, keep, base, f);
+    } else {
+      const uint4 ones = make_uint4(~0u, ~0u, ~0u, ~0u);
+      const uint4 b = valid ? bm : ones;
+      if constexpr (REDIRECT) {
+        const uint32_t at = valid ? base : dump;
+        if constexpr (NK > 0) walk_fast<NK, true, MUL>(row, b, NK, at, f);
+        else walk_fast<NMAX, false, MUL>(row, b, keep, at, f);
+      } else {
+        uint32_t r[KW];
 #pragma unroll
-      for (int j = 0; j < KW; ++j) row[j] = valid ? row[j] : 0u;
+        for (int j = 0; j < KW; ++j) r[j] = valid ? row[j] : 0u;
+        if constexpr (NK > 0) walk_fast<NK, true, MUL>(r, b, NK, base, f);
+        else walk_fast<NMAX, false, MUL>(r, b, keep, base, f);
+      }
     }
-    iters = keep;
-    return true;
+    return;
   }
   const uint32_t pc = valid ? pop : 0u;
   const uint32_t st = toff + wave_excl_scan(pc);
-  iters = (int)wave_uniform(wave_max_u32(pc));
-  load_row<KW>(rs, st, row_chunks(iters), true, row);
-  mask_row<KW>(row, pc);
-  if (!valid) bm = make_uint4(0u, 0u, 0u, 0u);
-  return false;
+  const int iters = (int)wave_uniform(wave_max_u32(pc));
+  uint32_t r[KW];
+  load_row<KW>(rs, st, row_chunks(iters), true, r);
+  mask_row<KW>(r, pc);
+  const uint4 b = valid ? bm : make_uint4(0u, 0u, 0u, 0u);
+  walk_general<NMAX, MUL>(r, b, iters, base, f);
 }
 
 }  // namespace mustafar

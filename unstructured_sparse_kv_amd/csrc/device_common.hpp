@@ -46,6 +46,11 @@ __device__ __forceinline__ uint32_t keep_if_lane_bit(uint64_t lane_mask, uint32_
   return r;
 }
 
+// 2^x with the hardware instruction alone (v_exp_f32): no rescaling of
+// arguments below -126, whose results only matter as (near-)zero
+// probabilities; exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
