@@ -92,9 +92,9 @@ def main() -> int:
                     help="layer caches the steps take turns over (>= 2 keeps them out of the LLC)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the hot path shards by (batch, kv head) with no exchange; see the sharding note "
-              "in the design document)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: every "
+              "(batch, kv head) unit of the decode step is independent, so more GPUs would each "
+              "run this same path on their own units", file=sys.stderr)
         return 2
 
     import numpy as np
