@@ -50,10 +50,13 @@ int check_device() {
 
 int launched(hipError_t e) { return e == hipSuccess ? MUSTAFAR_OK : MUSTAFAR_ELAUNCH; }
 
-int auto_splits(int64_t batch, int64_t hkv, int64_t max_seq_len) {
+// Sequence splits per (batch, kv head) when the caller passes 0: enough 4-wave
+// blocks to fill the device once -- two per compute unit for the sparse
+// kernels (their LDS footprint allows two), one for the dense kernel (measured
+// fastest) -- with at least two 64-row tiles per wave.
+int auto_splits(int64_t batch, int64_t hkv, int64_t max_seq_len, int64_t target_blocks = 512) {
   const int64_t units = batch * hkv;
   const int64_t tiles = (max_seq_len + 63) / 64;
-  const int64_t target_blocks = 512;  // two 4-wave blocks per compute unit (LDS-bound occupancy)
   int64_t s = (target_blocks + units - 1) / units;
   const int64_t most = (tiles + 2 * kDecodeWaves - 1) / (2 * kDecodeWaves);  // >= 2 tiles per wave
   if (s > most) s = most;
@@ -64,7 +67,8 @@ int auto_splits(int64_t batch, int64_t hkv, int64_t max_seq_len) {
 
 int decode_common_checks(const uint16_t* q, int32_t hq, int32_t batch, int32_t hkv, int32_t max_seq_len,
                          float scale, int32_t splits, const uint16_t* out, const void* ws,
-                         uint64_t ws_bytes, const int32_t* seq_lens, int* splits_out) {
+                         uint64_t ws_bytes, const int32_t* seq_lens, int* splits_out,
+                         int64_t target_blocks = 512) {
   if (!q || !out || !ws || !seq_lens) return MUSTAFAR_EINVAL;
   if (!aligned16(q) || !aligned16(out) || !aligned16(ws) || !aligned4(seq_lens))
     return MUSTAFAR_EINVAL;
@@ -75,7 +79,7 @@ int decode_common_checks(const uint16_t* q, int32_t hq, int32_t batch, int32_t h
   if (max_seq_len < 0 || splits < 0 || splits > kMaxSplits) return MUSTAFAR_EINVAL;
   if (!isfinite(scale)) return MUSTAFAR_EINVAL;
   if (batch > 65535 || hkv > 65535) return MUSTAFAR_EINVAL;  // grid z and y
-  const int sp = splits ? splits : auto_splits(batch, hkv, max_seq_len);
+  const int sp = splits ? splits : auto_splits(batch, hkv, max_seq_len, target_blocks);
   const uint64_t need = workspace_partial_bytes(batch, hq, sp);
   if (ws_bytes < need) return MUSTAFAR_ENOSPACE;
   *splits_out = sp;
@@ -249,7 +253,7 @@ int mustafar_dense_decode_attn(const uint16_t* q, int32_t num_q_heads, const uin
   if (t_stride <= 0 || t_stride * kHeadDim * 2 >= ((int64_t)1 << 32)) return MUSTAFAR_EINVAL;
   int sp = 0;
   int rc = decode_common_checks(q, num_q_heads, batch, num_kv_heads, max_seq_len, scale, splits,
-                                out, workspace, workspace_bytes, seq_lens, &sp);
+                                out, workspace, workspace_bytes, seq_lens, &sp, 256);
   if (rc) return rc;
   if ((rc = check_device())) return rc;
   DenseDecodeArgs a;
