@@ -81,6 +81,106 @@ def median(xs):
     return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
 
 
+def stack_sweep(args) -> int:
+    """The 32-layer Llama-3-8B-shaped stack: for B in {1,4,8,16,32,64} x T in
+    {16384, 65536, 131072}, the KV bytes of the whole stack against 288e9 B
+    (compressed and dense fp16) and, where the stack fits, the decode-attention
+    tokens/s = B / (32 x the per-layer decode-attention time).  The per-layer
+    time is measured over 3 layer caches of the point's shape taken in turn
+    (so each is read cold, as in a 32-layer decode step).  One sequence per T
+    is generated and pruned; the batch is filled with copies of its caches
+    (timing depends on the shapes and the per-row keep, not on the values)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import unstructured_sparse_kv_amd as usk
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    cfg = synth.CONFIGS["llama3_8b_stack"]
+    Hq, Hkv, d, L = cfg.Hq, cfg.Hkv, cfg.d, cfg.layers
+    keep = usk.keep_from_sparsity(cfg.sparsity)
+    budget = 288e9
+    NL = 3
+    scale = 1.0 / math.sqrt(d)
+
+    def per_layer_time(call, n_layers):
+        for i in range(n_layers):
+            call(i)
+        torch.cuda.synchronize()
+        ts = []
+        for j in range(2 * n_layers):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(j % n_layers)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return median(ts)
+
+    points = []
+    max_batch = {}
+    for T in (16384, 65536, 131072):
+        K1, V1, _, _ = synth.make_inputs(cfg, device=dev, layer=0, B=1, T=T)
+        seq1 = torch.full((1,), T, dtype=torch.int32, device=dev)
+        kc1, vc1 = usk.CompressedKV(1, Hkv, keep, T, dev), usk.CompressedKV(1, Hkv, keep, T, dev)
+        usk.prune_compress(kc1, K1, seq1)
+        usk.prune_compress(vc1, V1, seq1)
+        torch.cuda.synchronize()
+        comp_seq = (kc1.used_bytes([T]) + vc1.used_bytes([T])) * L
+        dense_seq = 2 * Hkv * T * d * 2 * L
+        max_batch[T] = {"compressed": int(budget // comp_seq), "dense": int(budget // dense_seq)}
+        for B in (1, 4, 8, 16, 32, 64):
+            pt = {"batch": B, "seq_len": T, "stack_kv_bytes_compressed": B * comp_seq,
+                  "stack_kv_bytes_dense": B * dense_seq, "fits_compressed": B * comp_seq <= budget,
+                  "fits_dense": B * dense_seq <= budget}
+            q = synth.normal_f16(cfg.seed, synth.S_Q, 0, (B, Hq, d), dev)
+            seq = torch.full((B,), T, dtype=torch.int32, device=dev)
+            out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+            if pt["fits_compressed"]:
+                layers = []
+                for _ in range(NL):
+                    kc, vc = usk.CompressedKV(B, Hkv, keep, T, dev), usk.CompressedKV(B, Hkv, keep, T, dev)
+                    for dst, src in ((kc, kc1), (vc, vc1)):
+                        for a, b in zip(dst.views(), src.views()):
+                            a.copy_(b.expand_as(a))
+                    layers.append((kc, vc))
+                ws = usk.make_workspace(B, Hq, Hkv, T)
+                t = per_layer_time(lambda i: usk.decode_attn(q, layers[i][0], layers[i][1], seq, T, scale,
+                                                             out, ws), NL)
+                pt["sparse_layer_us"] = round(t * 1e6, 2)
+                pt["sparse_tokens_per_s"] = round(B / (L * t), 1)
+                pt["sparse_gbs"] = round(B * comp_seq / L / t / 1e9, 1)
+                del layers, ws
+            if pt["fits_dense"]:
+                layers = []
+                for _ in range(NL):
+                    Kd = K1.expand(B, Hkv, T, d).contiguous()
+                    Vd = V1.expand(B, Hkv, T, d).contiguous()
+                    layers.append((Kd, Vd))
+                ws = usk.make_workspace(B, Hq, Hkv, T)
+                t = per_layer_time(lambda i: usk.dense_decode_attn(q, layers[i][0], layers[i][1], seq, T,
+                                                                   scale, out, ws), NL)
+                pt["dense_layer_us"] = round(t * 1e6, 2)
+                pt["dense_tokens_per_s"] = round(B / (L * t), 1)
+                del layers, ws
+            torch.cuda.empty_cache()
+            log(f"stack B={B} T={T}: " + ", ".join(f"{k}={v}" for k, v in pt.items()
+                                                   if k.endswith(("_us", "_per_s")) or k.startswith("fits")))
+            points.append(pt)
+        del K1, V1, kc1, vc1
+        torch.cuda.empty_cache()
+    res = {"metric": "32-layer stack: max batch in 288 GB (KV bytes) and decode-attention tokens/s",
+           "unit": "tokens/s", "n_gpus": 1, "dtype": "f16 in, f32 accumulate", "data": "synthetic",
+           "config": {"workload": "llama3_8b_stack: 32 layers, GQA 32/8, head_dim 128, keep 38 of 128",
+                      "layers_timed_in_turn": NL},
+           "max_batch_288GB": {str(k): v for k, v in max_batch.items()}, "points": points}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,6 +188,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--stack-sweep", action="store_true",
+                    help="instead of the benchmark: the 32-layer stack batch x length sweep")
     ap.add_argument("--layers", type=int, default=3,
                     help="layer caches the steps take turns over (>= 2 keeps them out of the LLC)")
     args = ap.parse_args()
@@ -96,6 +198,8 @@ def main() -> int:
               "(batch, kv head) unit of the decode step is independent, so more GPUs would each "
               "run this same path on their own units", file=sys.stderr)
         return 2
+    if args.stack_sweep:
+        return stack_sweep(args)
 
     import numpy as np
     import torch

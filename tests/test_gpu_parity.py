@@ -217,6 +217,41 @@ def test_llama3_layer_sampled(gpu):
     assert_attn_close(got, np.stack([refd[p] for p in pairs]), "llama3 dense")
 
 
+def test_llama3_stack_sampled(gpu):
+    """32-layer stack at its smallest sweep point (B=1, T=16384): every layer is
+    generated, pruned, compressed and attended on the GPU; three layers are
+    checked against the oracle (sampled kv heads bit-exact, sampled q heads
+    within tolerance, both sparse kernels)."""
+    cfg = synth.CONFIGS["llama3_8b_stack"]
+    keep = usk.keep_from_sparsity(cfg.sparsity)
+    B, T, G = cfg.B, cfg.T, cfg.Hq // cfg.Hkv
+    checks = {0: [(0, 0), (0, 31)], 13: [(0, 9)], cfg.layers - 1: [(0, 22), (0, 3)]}
+    seq_d = torch.full((B,), T, dtype=torch.int32, device=gpu)
+    for layer in range(cfg.layers):
+        K, V, q, _ = synth.make_inputs(cfg, device=gpu, layer=layer)
+        kc = compress_on_gpu(K, seq_d, keep, T)
+        vc = compress_on_gpu(V, seq_d, keep, T)
+        outs = {v: _decode(q, kc, vc, seq_d, T, 0, v) for v in SPARSE}
+        assert all(torch.isfinite(o.float()).all() for o in outs.values()), f"layer {layer}"
+        if layer not in checks:
+            continue
+        say(f"stack: layer {layer} oracle check")
+        pairs = checks[layer]
+        Kcpu, Vcpu, qcpu = K.cpu(), V.cpu(), q.cpu()
+        seq = np.full(B, T, np.int32)
+        units = sorted({(b, hq // G) for b, hq in pairs})
+        for b, h in units:
+            s1 = np.array([T], np.int32)
+            ko = oracle.compress(Kcpu[b:b + 1, h:h + 1], s1, keep, T)
+            vo = oracle.compress(Vcpu[b:b + 1, h:h + 1], s1, keep, T)
+            assert_compressed_equal(kc, ko, seq, [(b, h)], [(0, 0)])
+            assert_compressed_equal(vc, vo, seq, [(b, h)], [(0, 0)])
+        ref = oracle_attention_units(qcpu, Kcpu, Vcpu, seq, keep, keep, T, pairs, G)
+        for v, out in outs.items():
+            got = np.stack([_f64(out[b, hq]) for b, hq in pairs])
+            assert_attn_close(got, np.stack([ref[p] for p in pairs]), f"stack layer {layer} {v}")
+
+
 def test_ragged_append_sequence(gpu):
     cfg = synth.CONFIGS["mistral_ragged_append"]
     keep = usk.keep_from_sparsity(cfg.sparsity)
