@@ -73,7 +73,10 @@ typedef enum {
  *                min(64*j, T) * keep.
  *
  * capacity is the number of rows allocated per (batch, head): a positive
- * multiple of 64.  keep (0..head_dim) is the number of survivors per row.
+ * multiple of 64, at most 2^24, with capacity * keep * 2 < 2^31.  keep
+ * (0..head_dim) is the number of survivors per row.  head_dim must be 128.
+ * batch * num_kv_heads must stay below 2^31.  Calls that break these limits
+ * return MUSTAFAR_EINVAL (MUSTAFAR_EUNSUPPORTED for another head_dim).
  */
 typedef struct {
   int32_t batch;

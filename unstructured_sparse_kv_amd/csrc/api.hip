@@ -20,6 +20,7 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 int check_kv_shape(const mustafar_kv_t* kv) {
   if (!kv) return MUSTAFAR_EINVAL;
   if (kv->batch <= 0 || kv->num_kv_heads <= 0) return MUSTAFAR_EINVAL;
+  if ((int64_t)kv->batch * kv->num_kv_heads > INT32_MAX) return MUSTAFAR_EINVAL;  // unit index is 32-bit
   if (kv->head_dim <= 0) return MUSTAFAR_EINVAL;
   if (kv->head_dim != kHeadDim) return MUSTAFAR_EUNSUPPORTED;
   if (kv->keep < 0 || kv->keep > kv->head_dim) return MUSTAFAR_EINVAL;

@@ -63,36 +63,48 @@ __device__ __forceinline__ void store_row(const RowMask& m, uint32_t x0, uint32_
 
 constexpr int kPruneBlock = 256;
 constexpr int kWavesPerBlock = kPruneBlock / kWave;
+constexpr int kRowsPerWave = kTile / kWavesPerBlock;  // 16
 
+// Grid (64-row tiles, units); wave w of a block prunes rows
+// tile * 64 + 16w .. + 15 of its (batch, kv head) unit, one row at a time with
+// the next row's loads in flight.  Units beyond gridDim.y are taken in steps
+// of gridDim.y.  Row indices stay 32-bit within a unit.
 __global__ __launch_bounds__(kPruneBlock) void prune_compress_kernel(
     const uint16_t* __restrict__ dense, int64_t t_stride, const int32_t* __restrict__ seq_lens,
-    int32_t H, int32_t keep, int32_t cap, int64_t rows_per_unit, int64_t total_rows,
+    int32_t H, int32_t keep, int32_t cap, int32_t rows_per_unit, int32_t units,
     uint64_t* __restrict__ bitmaps, uint16_t* __restrict__ values,
     uint32_t* __restrict__ tile_off) {
   const uint32_t lane = lane_id();
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  const int64_t ntoff = cap / kTile + 1;
-  for (int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + wave_uniform((int)(threadIdx.x / kWave)); r < total_rows;
-       r += nwaves) {
-    const int64_t unit = r / rows_per_unit;
-    const int64_t t = r - unit * rows_per_unit;
-    const int64_t b = unit / H;
-    int64_t T = seq_lens[b];
-    T = T < 0 ? 0 : T;
-    T = T > rows_per_unit ? rows_per_unit : T;  // rows_per_unit = min(t_stride, cap)
-    uint32_t* toff = tile_off + unit * ntoff;
-    if (t == 0 && T == 0) {
-      if (lane == 0) toff[0] = 0;
-      continue;
-    }
-    if (t >= T) continue;
-    const uint16_t* src = dense + (unit * t_stride + t) * kHeadDim;
-    const uint32_t x0 = src[lane], x1 = src[lane + 64];
-    const RowMask m = select_row(x0, x1, keep);
-    store_row(m, x0, x1, bitmaps + (unit * cap + t) * 2, values + unit * (int64_t)cap * keep + t * keep);
-    if (lane == 0) {
-      if (t % kTile == 0) toff[t / kTile] = (uint32_t)(t * keep);
-      if (t == T - 1) toff[(T + kTile - 1) / kTile] = (uint32_t)(T * keep);
+  const int wave = wave_uniform((int)(threadIdx.x / kWave));
+  const int tile = blockIdx.x;
+  const int ntoff = cap / kTile + 1;
+  for (int unit = blockIdx.y; unit < units; unit += gridDim.y) {
+    int T = seq_lens[unit / H];
+    T = T < 0 ? 0 : (T > rows_per_unit ? rows_per_unit : T);
+    uint32_t* toff = tile_off + (int64_t)unit * ntoff;
+    if (tile == 0 && wave == 0 && lane == 0 && T == 0) toff[0] = 0;
+    const int t0 = tile * kTile + wave * kRowsPerWave;
+    const int tend = min(t0 + kRowsPerWave, T);
+    if (t0 >= tend) continue;
+    const uint16_t* src = dense + ((int64_t)unit * t_stride + t0) * kHeadDim;
+    uint64_t* bm = bitmaps + ((int64_t)unit * cap + t0) * 2;
+    uint16_t* vals = values + (int64_t)unit * cap * keep + (int64_t)t0 * keep;
+    uint32_t x0 = src[lane], x1 = src[lane + 64];
+    for (int t = t0; t < tend; ++t) {
+      // next row's loads (the last row reloads itself)
+      const int64_t step = (t + 1 < tend) ? kHeadDim : 0;
+      const uint32_t y0 = src[step + lane], y1 = src[step + lane + 64];
+      const RowMask m = select_row(x0, x1, keep);
+      store_row(m, x0, x1, bm, vals);
+      if (lane == 0) {
+        if (t % kTile == 0) toff[t / kTile] = (uint32_t)(t * keep);
+        if (t == T - 1) toff[(T + kTile - 1) / kTile] = (uint32_t)(T * keep);
+      }
+      src += step;
+      bm += 2;
+      vals += keep;
+      x0 = y0;
+      x1 = y1;
     }
   }
 }
@@ -146,13 +158,13 @@ __global__ __launch_bounds__(1024) void append_kernel(
 hipError_t launch_prune_compress(const mustafar_kv_t& d, const uint16_t* dense, int64_t t_stride,
                                  const int32_t* seq_lens, hipStream_t stream) {
   const int64_t rows_per_unit = t_stride < d.capacity ? t_stride : d.capacity;
-  const int64_t total = (int64_t)d.batch * d.num_kv_heads * rows_per_unit;
-  int64_t blocks = (total + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks > 256 * 128) blocks = 256 * 128;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(prune_compress_kernel, dim3((unsigned)blocks), dim3(kPruneBlock), 0, stream,
-                     dense, t_stride, seq_lens, d.num_kv_heads, d.keep, d.capacity, rows_per_unit,
-                     total, d.bitmaps, d.values, d.tile_offsets);
+  const int64_t units = (int64_t)d.batch * d.num_kv_heads;
+  const int64_t tiles = (rows_per_unit + kTile - 1) / kTile;
+  if (units <= 0 || tiles <= 0) return hipSuccess;
+  const unsigned gy = (unsigned)(units < 65535 ? units : 65535);
+  hipLaunchKernelGGL(prune_compress_kernel, dim3((unsigned)tiles, gy), dim3(kPruneBlock), 0, stream,
+                     dense, t_stride, seq_lens, d.num_kv_heads, d.keep, d.capacity,
+                     (int32_t)rows_per_unit, (int32_t)units, d.bitmaps, d.values, d.tile_offsets);
   return hipGetLastError();
 }
 
