@@ -77,6 +77,9 @@ typedef enum {
  * (0..head_dim) is the number of survivors per row.  head_dim must be 128.
  * batch * num_kv_heads must stay below 2^31.  Calls that break these limits
  * return MUSTAFAR_EINVAL (MUSTAFAR_EUNSUPPORTED for another head_dim).
+ * The decode calls also accept rows holding fewer than keep values (values
+ * still packed back to back, tile_offsets consistent with the popcounts);
+ * rows must not hold more than keep.
  */
 typedef struct {
   int32_t batch;

@@ -304,6 +304,78 @@ def test_ragged_append_sequence(gpu):
     assert status.item() == 0
 
 
+def _thin_rows(c: "oracle.Compressed", seq, rng):
+    """Rewrites an oracle-compressed tensor so that some rows hold fewer than
+    keep values: random rows lose their highest 1..10 set bits, some rows lose
+    a whole bitmap word, one row of the first tile loses one value (so later
+    tiles start at odd offsets).  Values stay packed back to back and tile
+    offsets are recomputed from the popcounts, as the format defines them."""
+    B, H, cap, k = c.B, c.H, c.cap, c.k
+    out = oracle.Compressed(B, H, cap, c.d, k)
+    for b in range(B):
+        T = int(seq[b])
+        for h in range(H):
+            src = c.values[b, h]
+            pos = 0
+            dst = []
+            toff = []
+            for r in range(T):
+                if r % 64 == 0:
+                    toff.append(len(dst))
+                words = [int(w) for w in c.bitmaps[b, h, r]]
+                bits = [64 * w + j for w in range(len(words)) for j in range(64) if (words[w] >> j) & 1]
+                vals = list(src[pos:pos + len(bits)])
+                pos += len(bits)
+                keep_idx = list(range(len(bits)))
+                u = rng.random()
+                if u < 0.3:
+                    keep_idx = keep_idx[:max(0, len(bits) - int(rng.integers(1, 11)))]
+                elif u < 0.4:
+                    lo, hi = (0, 32) if rng.random() < 0.5 else (96, 128)
+                    keep_idx = [i for i in keep_idx if not lo <= bits[i] < hi]
+                if r == 63 and (len(dst) + len(keep_idx)) % 2 == 0 and keep_idx:
+                    keep_idx = keep_idx[:-1]  # the second tile starts at an odd offset
+                nw = [0] * len(words)
+                for i in keep_idx:
+                    nw[bits[i] // 64] |= 1 << (bits[i] % 64)
+                    dst.append(vals[i])
+                out.bitmaps[b, h, r] = np.array(nw, dtype=np.uint64)
+            toff.append(len(dst))
+            out.values[b, h, :len(dst)] = np.array(dst, dtype=np.uint16)
+            out.tile_off[b, h, :len(toff)] = np.array(toff, dtype=np.uint32)
+    return out
+
+
+def _upload(c: "oracle.Compressed", gpu):
+    kv = usk.CompressedKV(c.B, c.H, c.k, c.cap, gpu)
+    bm, vals, toff = kv.views()
+    bm.copy_(torch.from_numpy(c.bitmaps.view(np.int64)))
+    vals.copy_(torch.from_numpy(c.values.view(np.int16)))
+    toff.copy_(torch.from_numpy(c.tile_off.view(np.int32)))
+    return kv
+
+
+@pytest.mark.parametrize("keep", [38, 64, 37])
+def test_rows_below_keep(gpu, keep):
+    """Caches whose rows hold fewer than keep values (and tiles starting at odd
+    offsets) take the exact-start path of both sparse kernels."""
+    B, Hq, Hkv, T, cap = 2, 4, 2, 300, 320
+    K, V, q = _small_inputs(B, Hq, Hkv, T, 4242 + keep)
+    seq = np.array([300, 130], np.int32)
+    rng = np.random.default_rng(keep)
+    ko = _thin_rows(oracle.compress(K, seq, keep, cap), seq, rng)
+    vo = _thin_rows(oracle.compress(V, seq, keep, cap), seq, rng)
+    assert ko.tile_off[0, 0, 1] % 2 == 1, "the second tile should start at an odd offset"
+    say(f"rows below keep: keep={keep}")
+    kc, vc = _upload(ko, gpu), _upload(vo, gpu)
+    seq_d = torch.from_numpy(seq).to(gpu)
+    ref = oracle.attention_compressed(q, ko, vo, seq, SCALE)
+    for variant in SPARSE:
+        for splits in (0, 2):
+            out = _decode(q.to(gpu), kc, vc, seq_d, T, splits, variant)
+            assert_attn_close(_f64(out), ref, f"rows below keep={keep} {variant} splits={splits}")
+
+
 def test_edge_cases(gpu):
     B, Hq, Hkv, T = 4, 4, 2, 130
     K, V, q = _small_inputs(B, Hq, Hkv, T, 7)
