@@ -163,9 +163,9 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
     // ---- key tile K[t][c]
     wave_lds_sync();  // the previous tile's reads of the buffer are done
 #pragma unroll
-    for (int j = 0; j < 16; ++j)  // 4 rows of 256 B per instruction; the row padding stays as is
-      *reinterpret_cast<uint4*>(tile_lds + (4 * j + (lane >> 4)) * kKRow + 16 * (lane & 15u)) =
-          make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < 32; ++j)  // 2 rows of 256 B per instruction; the row padding stays as is
+      *reinterpret_cast<uint2*>(tile_lds + (2 * j + (lane >> 5)) * kKRow + 8 * (lane & 31u)) =
+          make_uint2(0u, 0u);
     wave_lds_sync();
     decode_side<NMAX, NK, true, 2u>(krs, kt0, kk, valid, partial, !kEvenExact || !(kt0 & 1u), kb,
                                     krow, tile_base + lane * kKRow, tile_base + kKDump, scatter);
@@ -237,9 +237,9 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
     // ---- value tile V[c][t] in the same buffer
     wave_lds_sync();  // score reads of the key tile done; p written
 #pragma unroll
-    for (int j = 0; j < 16; ++j)  // 8 channel rows of 128 B per instruction
-      *reinterpret_cast<uint4*>(tile_lds + (8 * j + (lane >> 3)) * kVRow + 16 * (lane & 7u)) =
-          make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < 32; ++j)  // 4 channel rows of 128 B per instruction
+      *reinterpret_cast<uint2*>(tile_lds + (4 * j + (lane >> 4)) * kVRow + 8 * (lane & 15u)) =
+          make_uint2(0u, 0u);
     wave_lds_sync();
     decode_side<NMAX, NK, true, kVRow>(vrs, vt0, vk, valid, partial, !kEvenExact || !(vt0 & 1u), vb,
                                        vrow, tile_base + 2u * lane, tile_base + kVDump, scatter);
