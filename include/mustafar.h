@@ -145,8 +145,10 @@ int mustafar_prune_compress(const mustafar_kv_t *dst, const uint16_t *dense, int
  * (batch, kv head) by the same rule and store them as row T_b = seq_lens[b] of
  * `k` and `v`, then increment seq_lens[b] once ([Summary] "Approach" and
  * [Abstract]: the tokens produced during decode are pruned and compressed at
- * run time).  k and v must agree in batch, num_kv_heads and capacity and may
- * differ in keep.
+ * run time).  The row's values go right after the stored ones (at the tile
+ * offsets' end entry, T_b * keep when every row holds keep values) and the end
+ * entry advances by keep.  k and v must agree in batch, num_kv_heads and
+ * capacity and may differ in keep.
  *
  *   k_new, v_new (device) uint16 [batch][num_kv_heads][128] fp16 bits.
  *   seq_lens     (device) int32 [batch], incremented in place.
@@ -233,6 +235,31 @@ int mustafar_decode_attn_valu(const uint16_t *q, int32_t num_q_heads, const must
                               const mustafar_kv_t *v, const int32_t *seq_lens, int32_t max_seq_len,
                               float scale, int32_t splits, uint16_t *out, void *workspace,
                               uint64_t workspace_bytes, void *stream);
+
+/*
+ * One fused decode step: mustafar_append_token followed by mustafar_decode_attn
+ * in two kernel launches instead of three, with the same results bit for bit
+ * (caches, seq_lens, status and out).  The pages ask that the attention over
+ * the compressed caches pay for the run-time pruning and compression of the
+ * tokens produced during decode ([Abstract]; [Summary] "Approach"); here the
+ * wave whose tiles end the sequence prunes and stores the new key and value
+ * rows itself and attends over them in the same pass, and the merge kernel
+ * advances seq_lens.
+ *
+ *   k_new, v_new (device) uint16 [batch][num_kv_heads][128] fp16 bits (16 B aligned).
+ *   seq_lens     (device) int32 [batch]: row seq_lens[b] is added, attention covers
+ *                seq_lens[b] + 1 rows, and seq_lens[b] is incremented once.  A
+ *                sequence already at capacity adds nothing, attends over its
+ *                capacity rows and ORs MUSTAFAR_STATUS_APPEND_FULL into *status.
+ *   status       (device) uint32, may be NULL.
+ *   max_seq_len  host upper bound of the lengths after the step (picks splits).
+ *   Other arguments and errors as mustafar_decode_attn; the caches are written.
+ */
+int mustafar_decode_step(const uint16_t *q, int32_t num_q_heads, const mustafar_kv_t *k,
+                         const mustafar_kv_t *v, const uint16_t *k_new, const uint16_t *v_new,
+                         int32_t *seq_lens, uint32_t *status, int32_t max_seq_len, float scale,
+                         int32_t splits, uint16_t *out, void *workspace, uint64_t workspace_bytes,
+                         void *stream);
 
 /*
  * The same attention over dense, unpruned fp16 caches: the comparison

@@ -252,7 +252,50 @@ def test_llama3_stack_sampled(gpu):
             assert_attn_close(got, np.stack([ref[p] for p in pairs]), f"stack layer {layer} {v}")
 
 
-def test_ragged_append_sequence(gpu):
+@pytest.mark.parametrize("keep", [38, 64, 37])
+def test_decode_step_matches_separate_calls(gpu, keep):
+    """The fused step (mustafar_decode_step) against mustafar_append_token +
+    mustafar_decode_attn on copies of the same caches: out, caches, seq_lens
+    and status bit for bit, over steps that start a tile, fill an empty
+    sequence, and hit capacity."""
+    B, Hq, Hkv, T, cap = 4, 8, 2, 320, 320
+    K, V, q = _small_inputs(B, Hq, Hkv, T, 777 + keep)
+    seq0 = np.array([130, 64, 0, 318], np.int32)
+    say(f"fused step vs separate calls: keep={keep}")
+    seq_a = torch.from_numpy(seq0).to(gpu)
+    seq_b = seq_a.clone()
+    ka = compress_on_gpu(K.to(gpu), seq_a, keep, cap)
+    va = compress_on_gpu(V.to(gpu), seq_a, keep, cap)
+    kb_, vb_ = usk.CompressedKV(B, Hkv, keep, cap, gpu), usk.CompressedKV(B, Hkv, keep, cap, gpu)
+    for dst, src in ((kb_, ka), (vb_, va)):
+        for x, y in zip(dst.views(), src.views()):
+            x.copy_(y)
+    st_a = torch.zeros(1, dtype=torch.int32, device=gpu)
+    st_b = torch.zeros(1, dtype=torch.int32, device=gpu)
+    ws_a = usk.make_workspace(B, Hq, Hkv, cap)
+    ws_b = usk.make_workspace(B, Hq, Hkv, cap)
+    g = torch.Generator().manual_seed(keep)
+    for step in range(4):
+        kn = torch.randn(B, Hkv, 128, generator=g).half().to(gpu)
+        vn = torch.randn(B, Hkv, 128, generator=g).half().to(gpu)
+        qs = torch.randn(B, Hq, 128, generator=g).half().to(gpu)
+        out_a = torch.empty((B, Hq, 128), dtype=torch.float16, device=gpu)
+        out_b = torch.empty_like(out_a)
+        usk.append_token(ka, va, kn, vn, seq_a, st_a)
+        usk.decode_attn(qs, ka, va, seq_a, cap, SCALE, out_a, ws_a)
+        usk.decode_step(qs, kb_, vb_, kn, vn, seq_b, cap, SCALE, out_b, ws_b, st_b)
+        torch.cuda.synchronize()
+        assert torch.equal(seq_a, seq_b), f"step {step}: seq_lens {seq_a.tolist()} vs {seq_b.tolist()}"
+        assert st_a.item() == st_b.item(), f"step {step}: status"
+        assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16)), f"step {step}: out differs"
+        for name, c1, c2 in (("k", ka, kb_), ("v", va, vb_)):
+            for part, x, y in zip(("bitmaps", "values", "tile offsets"), c1.views(), c2.views()):
+                assert torch.equal(x, y), f"step {step}: {name} {part} differ"
+    assert seq_b.tolist() == [134, 68, 4, 320] and st_b.item() == usk.STATUS_APPEND_FULL
+
+
+@pytest.mark.parametrize("mode", ["separate", "fused"])
+def test_ragged_append_sequence(gpu, mode):
     cfg = synth.CONFIGS["mistral_ragged_append"]
     keep = usk.keep_from_sparsity(cfg.sparsity)
     seq0 = synth.seq_lens_uniform(cfg.seed, cfg.B, *cfg.ragged)
@@ -272,9 +315,12 @@ def test_ragged_append_sequence(gpu):
     check_steps = {1, 2, 32, cfg.steps}
     for step in range(1, cfg.steps + 1):
         kn, vn, q = synth.step_inputs(cfg, step - 1, device=gpu)
-        usk.append_token(kc, vc, kn, vn, seq_d, status)
-        usk.decode_attn(q, kc, vc, seq_d, cap, SCALE, out, ws)
-        usk.decode_attn_valu(q, kc, vc, seq_d, cap, SCALE, outv, ws)
+        if mode == "fused":
+            usk.decode_step(q, kc, vc, kn, vn, seq_d, cap, SCALE, out, ws, status)
+        else:
+            usk.append_token(kc, vc, kn, vn, seq_d, status)
+            usk.decode_attn(q, kc, vc, seq_d, cap, SCALE, out, ws)
+            usk.decode_attn_valu(q, kc, vc, seq_d, cap, SCALE, outv, ws)
         # the oracle sees the same new rows written into its dense copy
         T_old = seq0 + (step - 1)
         for b in range(cfg.B):
@@ -300,7 +346,8 @@ def test_ragged_append_sequence(gpu):
                     assert_compressed_equal(kc, ko, seq_now, [(b, h)], [(0, 0)])
                     assert_compressed_equal(vc, vo, seq_now, [(b, h)], [(0, 0)])
             assert_attn_close(np.stack(got), np.stack(exp), f"ragged append step {step}")
-            assert_attn_close(np.stack(gotv), np.stack(exp), f"ragged append step {step} valu")
+            if mode == "separate":
+                assert_attn_close(np.stack(gotv), np.stack(exp), f"ragged append step {step} valu")
     assert status.item() == 0
 
 

@@ -28,7 +28,7 @@ EXPORTS = (
     "mustafar_kv_used_bytes", "mustafar_prune_compress", "mustafar_append_token",
     "mustafar_decode_auto_splits", "mustafar_decode_workspace_bytes",
     "mustafar_decode_workspace_init", "mustafar_decode_attn", "mustafar_decode_attn_valu",
-    "mustafar_dense_decode_attn", "mustafar_probe_stream_read",
+    "mustafar_decode_step", "mustafar_dense_decode_attn", "mustafar_probe_stream_read",
 )
 
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
                                                     P, U64, P]),
             "mustafar_decode_attn_valu": (ctypes.c_int, [P, I32, KVP, KVP, P, I32, ctypes.c_float,
                                                          I32, P, P, U64, P]),
+            "mustafar_decode_step": (ctypes.c_int, [P, I32, KVP, KVP, P, P, P, P, I32, ctypes.c_float,
+                                                    I32, P, P, U64, P]),
             "mustafar_dense_decode_attn": (ctypes.c_int, [P, I32, P, P, I32, I32, I32, I64, P, I32,
                                                           ctypes.c_float, I32, P, P, U64, P]),
             "mustafar_probe_stream_read": (ctypes.c_int, [P, U64, P, P]),
@@ -204,6 +206,18 @@ def decode_attn_valu(q, k: CompressedKV, v: CompressedKV, seq_lens, max_seq_len:
     _check("mustafar_decode_attn_valu", lib().mustafar_decode_attn_valu(
         q.data_ptr(), q.shape[1], k.ref, v.ref, seq_lens.data_ptr(), max_seq_len, scale, splits,
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def decode_step(q, k: CompressedKV, v: CompressedKV, k_new, v_new, seq_lens, max_seq_len: int,
+                scale: float, out, workspace, status=None, splits: int = 0, stream=None) -> None:
+    """Fused append + decode: k_new / v_new [B][Hkv][128] fp16 become row seq_lens[b],
+    the attention covers it, seq_lens advances (device tensors)."""
+    assert q.is_contiguous() and out.is_contiguous()
+    assert k_new.is_contiguous() and v_new.is_contiguous()
+    _check("mustafar_decode_step", lib().mustafar_decode_step(
+        q.data_ptr(), q.shape[1], k.ref, v.ref, k_new.data_ptr(), v_new.data_ptr(),
+        seq_lens.data_ptr(), _ptr(status), max_seq_len, scale, splits, out.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
 
 
 def dense_decode_attn(q, k, v, seq_lens, max_seq_len: int, scale: float, out, workspace,

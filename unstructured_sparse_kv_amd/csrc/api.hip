@@ -90,10 +90,14 @@ int decode_common_checks(const uint16_t* q, int32_t hq, int32_t batch, int32_t h
 
 typedef hipError_t (*SparseLauncher)(const SparseDecodeArgs&, int, hipStream_t);
 
+// Decode over the compressed caches; with k_new / v_new (the fused step) the
+// split kernel first stores the new rows and the merge kernel advances seq_lens.
 int sparse_decode(SparseLauncher launch, const uint16_t* q, int32_t num_q_heads,
                   const mustafar_kv_t* k, const mustafar_kv_t* v, const int32_t* seq_lens,
                   int32_t max_seq_len, float scale, int32_t splits, uint16_t* out,
-                  void* workspace, uint64_t workspace_bytes, void* stream) {
+                  void* workspace, uint64_t workspace_bytes, void* stream,
+                  const uint16_t* k_new = nullptr, const uint16_t* v_new = nullptr,
+                  uint32_t* status = nullptr) {
   int rc = check_kv(k);
   if (rc) return rc;
   if ((rc = check_kv(v))) return rc;
@@ -121,9 +125,13 @@ int sparse_decode(SparseLauncher launch, const uint16_t* q, int32_t num_q_heads,
   a.seq_lens = seq_lens;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   a.part = (float*)workspace;
+  a.k_new = k_new;
+  a.v_new = v_new;
   hipStream_t st = (hipStream_t)stream;
   if ((rc = launched(launch(a, k->batch, st)))) return rc;
-  return launched(launch_decode_reduce(a.part, k->batch, num_q_heads, k->num_kv_heads, sp, out, st));
+  return launched(launch_decode_reduce(a.part, k->batch, num_q_heads, k->num_kv_heads, sp, out, st,
+                                       const_cast<int32_t*>(seq_lens), status, k->capacity,
+                                       k_new != nullptr));
 }
 
 }  // namespace
@@ -242,6 +250,17 @@ int mustafar_decode_attn_valu(const uint16_t* q, int32_t num_q_heads, const must
                               uint64_t workspace_bytes, void* stream) {
   return sparse_decode(launch_decode_sparse_valu, q, num_q_heads, k, v, seq_lens, max_seq_len,
                        scale, splits, out, workspace, workspace_bytes, stream);
+}
+
+int mustafar_decode_step(const uint16_t* q, int32_t num_q_heads, const mustafar_kv_t* k,
+                         const mustafar_kv_t* v, const uint16_t* k_new, const uint16_t* v_new,
+                         int32_t* seq_lens, uint32_t* status, int32_t max_seq_len, float scale,
+                         int32_t splits, uint16_t* out, void* workspace, uint64_t workspace_bytes,
+                         void* stream) {
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return MUSTAFAR_EINVAL;
+  if (status && !aligned4(status)) return MUSTAFAR_EINVAL;
+  return sparse_decode(launch_decode_sparse, q, num_q_heads, k, v, seq_lens, max_seq_len, scale,
+                       splits, out, workspace, workspace_bytes, stream, k_new, v_new, status);
 }
 
 int mustafar_dense_decode_attn(const uint16_t* q, int32_t num_q_heads, const uint16_t* k,

@@ -32,6 +32,7 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "merge.hpp"
+#include "select_row.hpp"
 
 namespace mustafar {
 namespace {
@@ -50,20 +51,46 @@ constexpr uint32_t kVDump = 128;
 static_assert(kKDump + kKRow <= (uint32_t)kTileBytes, "key dump row inside the tile buffer");
 constexpr float kRescaleSlack = 8.f;   // log2 units
 
-template <int G>
+template <int G, int KW>
 struct MfmaCfg {
   static constexpr int kPBytes = (G + 1) * 128;  // p[head][64] fp16; head row G stays zero
-  static constexpr int kWaveBytes = (kTileBytes + kPBytes + 15) / 16 * 16;
+  // fused decode step: the new key and value rows, packed (bitmap words, then
+  // the row registers' worth of values, zero past keep)
+  static constexpr int kNewSide = 16 + 4 * KW;
+  static constexpr int kNewBytes = 2 * kNewSide;
+  static constexpr int kWaveBytes = (kTileBytes + kPBytes + kNewBytes + 15) / 16 * 16;
   static constexpr int kMergeBytes = kDecodeWaves * G * (2 + kHeadDim) * 4;
   static constexpr int kLdsBytes =
       kDecodeWaves * kWaveBytes > kMergeBytes ? kDecodeWaves * kWaveBytes : kMergeBytes;
 };
 
+// Fused decode step: one wave prunes the new row of one side (lane l holds
+// channels l and l + 64 of `src`), stores it as row T of the compressed cache
+// (values right after the stored ones, at the tile offsets' end entry, which
+// then advances by keep) and keeps a packed copy at `copy` in LDS for the lane
+// that owns the row in the tile walk.
+template <int KW>
+__device__ __forceinline__ void append_row(const uint16_t* src, int keep, uint64_t* bm_unit,
+                                           uint16_t* val_unit, uint32_t* toff_unit, int T,
+                                           char* copy) {
+  const uint32_t lane = lane_id();
+  constexpr int kChunks = (16 + 4 * KW) / 16;
+  if (lane < (uint32_t)kChunks) *reinterpret_cast<uint4*>(copy + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t x0 = src[lane], x1 = src[lane + 64];
+  const RowMask m = select_row(x0, x1, keep);
+  const uint32_t pos = toff_unit[(T + kTile - 1) / kTile];
+  store_row(m, x0, x1, bm_unit + (int64_t)T * 2, val_unit + pos);
+  if (lane == 0) toff_unit[(T + kTile) / kTile] = pos + (uint32_t)keep;
+  wave_lds_sync();  // the zeroed copy before the packed row goes in
+  store_row(m, x0, x1, reinterpret_cast<uint64_t*>(copy), reinterpret_cast<uint16_t*>(copy + 16));
+  wave_lds_sync();
+}
+
 template <int G, int KMAX, int NK>
 __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
-  using C = MfmaCfg<G>;
   constexpr int NMAX = NK > 0 ? NK : KMAX;
   constexpr int KW = RowCfg<NMAX>::kW;
+  using C = MfmaCfg<G, KW>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -71,13 +98,16 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
   const int wave = wave_uniform((int)(threadIdx.x / kWave));
   const uint32_t lane = lane_id();
   const uint32_t l16 = lane & 15u, grp = lane >> 4;
-  int T = a.seq_lens[b];
-  T = T < 0 ? 0 : (T > a.cap ? a.cap : T);
+  int T_old = a.seq_lens[b];
+  T_old = T_old < 0 ? 0 : (T_old > a.cap ? a.cap : T_old);
+  const bool add = a.k_new != nullptr && T_old < a.cap;  // fused step adds row T_old
+  const int T = add ? T_old + 1 : T_old;
   const int ntiles = (T + kTile - 1) / kTile;
   const int ntoff = a.cap / kTile + 1;
 
   char* tile_lds = smem + wave * C::kWaveBytes;
   uint16_t* p_lds = reinterpret_cast<uint16_t*>(tile_lds + kTileBytes);  // [G + 1][64]
+  char* new_lds = tile_lds + kTileBytes + C::kPBytes;                    // new K row, new V row
   if (lane < 8u) *reinterpret_cast<uint4*>(p_lds + G * 64 + 8 * lane) = make_uint4(0u, 0u, 0u, 0u);
 
   // B operand of the score MFMA: query heads as columns (zero beyond G)
@@ -111,6 +141,30 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
   const auto vtrs = make_rsrc(a.vtoff + (int64_t)unit * ntoff, (uint32_t)ntoff * 4u);
   const int kch = row_chunks(kk), vch = row_chunks(vk);
   const bool k_odd = (kk & 1) != 0, v_odd = (vk & 1) != 0;
+
+  // fused step: the wave whose tiles include the new row stores it first; the
+  // lane that owns the row in the walk then takes it from the LDS copy (its
+  // prefetched bytes predate the store)
+  const int tile_new = T_old / kTile;
+  const bool owner = add && tile_new >= tb && tile_new < te;
+  const uint32_t new_lane = (uint32_t)(T_old - tile_new * kTile);
+  if (owner) {
+    const int64_t ubase = (int64_t)unit * a.cap;
+    append_row<KW>(a.k_new + (int64_t)unit * kHeadDim, kk, const_cast<uint64_t*>(a.kbm) + ubase * 2,
+                   const_cast<uint16_t*>(a.kval) + ubase * kk,
+                   const_cast<uint32_t*>(a.ktoff) + (int64_t)unit * ntoff, T_old, new_lds);
+    append_row<KW>(a.v_new + (int64_t)unit * kHeadDim, vk, const_cast<uint64_t*>(a.vbm) + ubase * 2,
+                   const_cast<uint16_t*>(a.vval) + ubase * vk,
+                   const_cast<uint32_t*>(a.vtoff) + (int64_t)unit * ntoff, T_old,
+                   new_lds + C::kNewSide);
+  }
+  auto take_new = [&](int tile, const char* copy, uint4& bm, uint32_t (&row)[KW]) {
+    if (owner && tile == tile_new && lane == new_lane) {
+      bm = *reinterpret_cast<const uint4*>(copy);
+#pragma unroll
+      for (int j = 0; j < KW; ++j) row[j] = reinterpret_cast<const uint32_t*>(copy + 16)[j];
+    }
+  };
 
   // tile offsets of this wave's tiles, 64 at a time, one per lane
   int toff_base = tb;
@@ -167,8 +221,10 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
       *reinterpret_cast<uint2*>(tile_lds + (2 * j + (lane >> 5)) * kKRow + 8 * (lane & 31u)) =
           make_uint2(0u, 0u);
     wave_lds_sync();
+    take_new(tile, new_lds, kb, krow);
     decode_side<NMAX, NK, true, 2u>(krs, kt0, kk, valid, partial, !kEvenExact || !(kt0 & 1u), kb,
-                                    krow, tile_base + lane * kKRow, tile_base + kKDump, scatter);
+                                    krow, tile_base + lane * kKRow, tile_base + kKDump, scatter,
+                                    [&](uint32_t (&r)[KW]) { uint4 t; take_new(tile, new_lds, t, r); });
     issue_k(nxt, kt0n);
     wave_lds_sync();
 
@@ -241,8 +297,11 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
       *reinterpret_cast<uint2*>(tile_lds + (4 * j + (lane >> 4)) * kVRow + 8 * (lane & 15u)) =
           make_uint2(0u, 0u);
     wave_lds_sync();
-    decode_side<NMAX, NK, true, kVRow>(vrs, vt0, vk, valid, partial, !kEvenExact || !(vt0 & 1u), vb,
-                                       vrow, tile_base + 2u * lane, tile_base + kVDump, scatter);
+    take_new(tile, new_lds + C::kNewSide, vb, vrow);
+    decode_side<NMAX, NK, true, kVRow>(
+        vrs, vt0, vk, valid, partial, !kEvenExact || !(vt0 & 1u), vb, vrow, tile_base + 2u * lane,
+        tile_base + kVDump, scatter,
+        [&](uint32_t (&r)[KW]) { uint4 t; take_new(tile, new_lds + C::kNewSide, t, r); });
     issue_v(nxt, vt0n);
     wave_lds_sync();
 
@@ -287,7 +346,7 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(Sparse
 
 template <int G, int KMAX, int NK>
 hipError_t launch_mfma_t(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
-  constexpr int lds = MfmaCfg<G>::kLdsBytes;
+  constexpr int lds = MfmaCfg<G, RowCfg<(NK > 0 ? NK : KMAX)>::kW>::kLdsBytes;
   if constexpr (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&decode_sparse_mfma_kernel<G, KMAX, NK>),

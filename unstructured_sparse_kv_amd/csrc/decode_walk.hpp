@@ -160,12 +160,18 @@ __device__ __forceinline__ uint32_t pop4(uint4 w) {
 // from their exact starts (prefix sum of the popcounts) into registers of
 // their own and walked by the general walk; lanes past the end walk nothing.
 // The prefetched registers are only read here, so the next prefetch can
-// overwrite them in place.
-template <int NMAX, int NK, bool REDIRECT, uint32_t MUL, int KW, class F>
+// overwrite them in place.  `patch` may overwrite rows of the reloaded
+// registers (a row whose stored bytes this kernel wrote itself).
+struct NoPatch {
+  template <int KW>
+  __device__ __forceinline__ void operator()(uint32_t (&)[KW]) const {}
+};
+
+template <int NMAX, int NK, bool REDIRECT, uint32_t MUL, int KW, class F, class P = NoPatch>
 __device__ __forceinline__ void decode_side(__amdgpu_buffer_rsrc_t rs, uint32_t toff, int keep,
                                             bool valid, bool partial, bool start_ok, uint4 bm,
                                             const uint32_t (&row)[KW], uint32_t base,
-                                            uint32_t dump, F&& f) {
+                                            uint32_t dump, F&& f, P&& patch = P()) {
   const uint32_t pop = pop4(bm);
   const bool lane_fast = !valid || (pop == (uint32_t)keep && bm.x && bm.y && bm.z && bm.w);
   if (start_ok && __ballot(!lane_fast) == 0ull) {
@@ -195,6 +201,7 @@ __device__ __forceinline__ void decode_side(__amdgpu_buffer_rsrc_t rs, uint32_t 
   uint32_t r[KW];
   load_row<KW>(rs, st, row_chunks(iters), true, r);
   mask_row<KW>(r, pc);
+  patch(r);
   const uint4 b = valid ? bm : make_uint4(0u, 0u, 0u, 0u);
   walk_general<NMAX, MUL>(r, b, iters, base, f);
 }

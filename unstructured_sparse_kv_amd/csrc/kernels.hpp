@@ -24,6 +24,11 @@ struct SparseDecodeArgs {
   const int32_t* seq_lens;
   float scale_log2;
   float* part;
+  // fused decode step: when set, the new key and value rows [B][Hkv][128] are
+  // pruned, compressed and stored as row seq_lens[b] before the attention,
+  // which then covers that row too (matrix-core kernel only)
+  const uint16_t* k_new;
+  const uint16_t* v_new;
 };
 
 struct DenseDecodeArgs {
@@ -50,8 +55,11 @@ hipError_t launch_append(const mustafar_kv_t& k, const mustafar_kv_t& v, const u
 hipError_t launch_decode_sparse(const SparseDecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_decode_sparse_valu(const SparseDecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_decode_dense(const DenseDecodeArgs& a, int batch, hipStream_t stream);
+// Merges the split partials into out; with `advance` (a fused decode step) it
+// also advances seq_lens[b] by one, or flags a full sequence in *status.
 hipError_t launch_decode_reduce(const float* part, int batch, int hq, int hkv, int splits,
-                                uint16_t* out, hipStream_t stream);
+                                uint16_t* out, hipStream_t stream, int32_t* seq_lens = nullptr,
+                                uint32_t* status = nullptr, int32_t cap = 0, bool advance = false);
 hipError_t launch_zero_u32(uint32_t* p, uint64_t n, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t stream);
 

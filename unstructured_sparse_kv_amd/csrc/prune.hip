@@ -4,62 +4,13 @@
 // pruning and compression of the tokens produced during decode), [README]
 // "Part II" (the token-wise, magnitude-based variant Kt_Mag / Vt_Mag).
 //
-// One wave owns one 128-channel row: lane l holds channels l and l + 64, so
-// "channel order" is "register 0 lanes, then register 1 lanes", which is the
-// order ballot and mbcnt count in.
+// One wave owns one 128-channel row (select_row.hpp).
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "select_row.hpp"
 
 namespace mustafar {
 namespace {
-
-struct RowMask {
-  uint64_t w0, w1;  // kept channels 0..63 and 64..127
-};
-
-// Survivors of one row: the `keep` largest magnitude keys (bits & 0x7FFF; finite
-// fp16 magnitudes order like these integers, and -0 == +0), ties to the lower
-// channel.  tau is found by an MSB-first bisection over the 15 key bits: the
-// largest value with #(key >= tau) >= keep, i.e. the keep-th largest key.  The
-// loop stops early once exactly `keep` keys are >= the candidate.
-__device__ __forceinline__ RowMask select_row(uint32_t x0, uint32_t x1, int keep) {
-  const uint32_t k0 = x0 & 0x7FFFu, k1 = x1 & 0x7FFFu;
-  uint32_t tau = 0;
-#pragma unroll
-  for (int b = 14; b >= 0; --b) {
-    const uint32_t cand = tau | (1u << b);
-    const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
-    if (cnt >= keep) tau = cand;
-    if (cnt == keep) break;
-  }
-  const uint64_t g0 = __ballot(k0 > tau), g1 = __ballot(k1 > tau);
-  const int need = keep - (__popcll(g0) + __popcll(g1));
-  const uint64_t e0 = __ballot(k0 == tau), e1 = __ballot(k1 == tau);
-  const int r0 = (int)mbcnt64(e0, 0u);
-  const int r1 = (int)mbcnt64(e1, (uint32_t)__popcll(e0));
-  const bool keep0 = (k0 > tau) || (k0 == tau && r0 < need);
-  const bool keep1 = (k1 > tau) || (k1 == tau && r1 < need);
-  return RowMask{__ballot(keep0), __ballot(keep1)};
-}
-
-// Writes the row's bitmap words and packs its kept values (ascending channel)
-// at `vals`.
-__device__ __forceinline__ void store_row(const RowMask& m, uint32_t x0, uint32_t x1,
-                                          uint64_t* bm_row, uint16_t* vals) {
-  const uint32_t lane = lane_id();
-  const uint32_t pos0 = mbcnt64(m.w0, 0u);
-  const uint32_t pos1 = mbcnt64(m.w1, (uint32_t)__popcll(m.w0));
-  if ((m.w0 >> lane) & 1ull) vals[pos0] = (uint16_t)x0;
-  if ((m.w1 >> lane) & 1ull) vals[pos1] = (uint16_t)x1;
-  if (lane == 0) {
-    uint4 w;
-    w.x = (uint32_t)m.w0;
-    w.y = (uint32_t)(m.w0 >> 32);
-    w.z = (uint32_t)m.w1;
-    w.w = (uint32_t)(m.w1 >> 32);
-    *reinterpret_cast<uint4*>(bm_row) = w;
-  }
-}
 
 constexpr int kPruneBlock = 256;
 constexpr int kWavesPerBlock = kPruneBlock / kWave;
@@ -133,14 +84,14 @@ __global__ __launch_bounds__(1024) void append_kernel(
       const uint16_t* src = (is_v ? v_new : k_new) + unit * kHeadDim;
       const uint32_t x0 = src[lane], x1 = src[lane + 64];
       const RowMask m = select_row(x0, x1, keep);
+      // the new row's values go right after the stored ones: the current end
+      // entry of the tile offsets (T * keep when every row holds keep values)
+      uint32_t* toff = (is_v ? vtoff : ktoff) + unit * ntoff;
+      const uint32_t pos = toff[(T + kTile - 1) / kTile];
       uint64_t* bm = (is_v ? vbm : kbm) + (unit * cap + T) * 2;
-      uint16_t* vals = (is_v ? vval : kval) + unit * (int64_t)cap * keep + (int64_t)T * keep;
+      uint16_t* vals = (is_v ? vval : kval) + unit * (int64_t)cap * keep + pos;
       store_row(m, x0, x1, bm, vals);
-      if (lane == 0) {
-        uint32_t* toff = (is_v ? vtoff : ktoff) + unit * ntoff;
-        if (T % kTile == 0) toff[T / kTile] = (uint32_t)((int64_t)T * keep);
-        toff[(T + kTile) / kTile] = (uint32_t)((int64_t)(T + 1) * keep);
-      }
+      if (lane == 0) toff[(T + kTile) / kTile] = pos + (uint32_t)keep;
     }
   }
   __syncthreads();

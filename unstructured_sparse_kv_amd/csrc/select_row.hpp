@@ -1,0 +1,63 @@
+// Per-token magnitude selection of one 128-channel row by one wave, and the
+// packing of its survivors (shared by the prune/append kernels and the fused
+// decode step).  Sources: [Summary] "Approach" (per-token magnitude pruning
+// into a bitmap-based format); [README] "Part II" (the token-wise,
+// magnitude-based variant).
+//
+// Lane l holds channels l and l + 64, so "channel order" is "register 0 lanes,
+// then register 1 lanes", which is the order ballot and mbcnt count in.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace mustafar {
+
+struct RowMask {
+  uint64_t w0, w1;  // kept channels 0..63 and 64..127
+};
+
+// Survivors of one row: the `keep` largest magnitude keys (bits & 0x7FFF; finite
+// fp16 magnitudes order like these integers, and -0 == +0), ties to the lower
+// channel.  tau is found by an MSB-first bisection over the 15 key bits: the
+// largest value with #(key >= tau) >= keep, i.e. the keep-th largest key.  The
+// loop stops early once exactly `keep` keys are >= the candidate.
+__device__ __forceinline__ RowMask select_row(uint32_t x0, uint32_t x1, int keep) {
+  const uint32_t k0 = x0 & 0x7FFFu, k1 = x1 & 0x7FFFu;
+  uint32_t tau = 0;
+#pragma unroll
+  for (int b = 14; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
+    if (cnt >= keep) tau = cand;
+    if (cnt == keep) break;
+  }
+  const uint64_t g0 = __ballot(k0 > tau), g1 = __ballot(k1 > tau);
+  const int need = keep - (__popcll(g0) + __popcll(g1));
+  const uint64_t e0 = __ballot(k0 == tau), e1 = __ballot(k1 == tau);
+  const int r0 = (int)mbcnt64(e0, 0u);
+  const int r1 = (int)mbcnt64(e1, (uint32_t)__popcll(e0));
+  const bool keep0 = (k0 > tau) || (k0 == tau && r0 < need);
+  const bool keep1 = (k1 > tau) || (k1 == tau && r1 < need);
+  return RowMask{__ballot(keep0), __ballot(keep1)};
+}
+
+// Writes the row's bitmap words and packs its kept values (ascending channel)
+// at `vals`.
+__device__ __forceinline__ void store_row(const RowMask& m, uint32_t x0, uint32_t x1,
+                                          uint64_t* bm_row, uint16_t* vals) {
+  const uint32_t lane = lane_id();
+  const uint32_t pos0 = mbcnt64(m.w0, 0u);
+  const uint32_t pos1 = mbcnt64(m.w1, (uint32_t)__popcll(m.w0));
+  if ((m.w0 >> lane) & 1ull) vals[pos0] = (uint16_t)x0;
+  if ((m.w1 >> lane) & 1ull) vals[pos1] = (uint16_t)x1;
+  if (lane == 0) {
+    uint4 w;
+    w.x = (uint32_t)m.w0;
+    w.y = (uint32_t)(m.w0 >> 32);
+    w.z = (uint32_t)m.w1;
+    w.w = (uint32_t)(m.w1 >> 32);
+    *reinterpret_cast<uint4*>(bm_row) = w;
+  }
+}
+
+}  // namespace mustafar

@@ -31,7 +31,10 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 __global__ __launch_bounds__(kHeadDim) void decode_reduce_kernel(const float* __restrict__ part,
                                                                  int hq_total, int g_size,
                                                                  int splits,
-                                                                 uint16_t* __restrict__ out) {
+                                                                 uint16_t* __restrict__ out,
+                                                                 int32_t* seq_lens,
+                                                                 uint32_t* status, int32_t cap,
+                                                                 int advance) {
   const int bq = blockIdx.x;
   const int b = bq / hq_total, hq = bq % hq_total;
   const int hkv = hq_total / g_size;
@@ -52,14 +55,25 @@ __global__ __launch_bounds__(kHeadDim) void decode_reduce_kernel(const float* __
     L += ps[1] * f;
   }
   out[(int64_t)bq * kHeadDim + c] = float_to_half_bits(L > 0.f ? A / L : 0.f);
+  // a fused decode step: the split kernel stored row seq_lens[b] (all its
+  // blocks read the old length); one thread per sequence now advances it
+  if (advance && hq == 0 && c == 0) {
+    const int32_t t = seq_lens[b] < 0 ? 0 : seq_lens[b];
+    if (t >= cap) {
+      if (status) atomicOr(status, MUSTAFAR_STATUS_APPEND_FULL);
+    } else {
+      seq_lens[b] = t + 1;
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode_reduce(const float* part, int batch, int hq, int hkv, int splits,
-                                uint16_t* out, hipStream_t stream) {
+                                uint16_t* out, hipStream_t stream, int32_t* seq_lens,
+                                uint32_t* status, int32_t cap, bool advance) {
   hipLaunchKernelGGL(decode_reduce_kernel, dim3(batch * hq), dim3(kHeadDim), 0, stream, part, hq,
-                     hq / hkv, splits, out);
+                     hq / hkv, splits, out, seq_lens, status, cap, advance ? 1 : 0);
   return hipGetLastError();
 }
 
