@@ -348,9 +348,7 @@ template <int G, int KMAX, int NK>
 hipError_t launch_mfma_t(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
   constexpr int lds = MfmaCfg<G, RowCfg<(NK > 0 ? NK : KMAX)>::kW>::kLdsBytes;
   if constexpr (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_sparse_mfma_kernel<G, KMAX, NK>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipError_t e = ensure_lds_limit<&decode_sparse_mfma_kernel<G, KMAX, NK>>(lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((decode_sparse_mfma_kernel<G, KMAX, NK>), dim3(a.splits, a.Hkv, batch),

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/mustafar.h"
 
 namespace mustafar {
@@ -41,6 +43,22 @@ struct DenseDecodeArgs {
   float scale_log2;
   float* part;
 };
+
+// Raises a kernel's dynamic LDS limit above the default 64 KB, once per device
+// (the host call is not free, so launches skip it after the first).
+template <auto Kernel>
+hipError_t ensure_lds_limit(int bytes) {
+  static std::atomic<uint64_t> configured{0};  // bit d: device d done (devices 0..63)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+  if (bit && (configured.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) configured.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 // Workspace: the split partials, [batch][Hkv][splits][G][kPartStride] fp32.
 inline uint64_t workspace_partial_bytes(int64_t batch, int64_t hq, int64_t splits) {
