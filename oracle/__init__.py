@@ -64,6 +64,16 @@ def lib():
         L.orc_attention_compressed.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, P, P, P, ctypes.c_int, P, P, P,
                                                ctypes.c_int, I64, P, F64, P, I64, P, ctypes.c_int]
+        Ci = ctypes.c_int
+        L.orc_compress_hk.restype = Ci
+        L.orc_compress_hk.argtypes = [P, Ci, Ci, I64, Ci, P, Ci, P, I64, P, P, P, Ci]
+        L.orc_decompress_hk.restype = Ci
+        L.orc_decompress_hk.argtypes = [P, P, P, Ci, Ci, I64, Ci, Ci, P, P, P]
+        L.orc_used_bytes_hk.restype = I64
+        L.orc_used_bytes_hk.argtypes = [Ci, Ci, P, I64, Ci, Ci, P]
+        L.orc_attention_compressed_hk.restype = Ci
+        L.orc_attention_compressed_hk.argtypes = [P, Ci, Ci, Ci, Ci, P, P, P, Ci, P, P, P, P, Ci, P,
+                                                  I64, P, F64, P, I64, P, Ci]
         _lib = L
     return _lib
 
@@ -107,26 +117,40 @@ def prune_rows(x, k: int) -> np.ndarray:
 
 
 class Compressed:
-    """One compressed tensor: bitmaps [B][H][cap][d/64] u64, values [B][H][cap*k] u16,
-    tile_off [B][H][cap/64+1] u32."""
+    """One compressed tensor: bitmaps [B][H][cap][d/64] u64, tile_off [B][H][cap/64+1] u32 and
+    values: [B][H][cap*k] u16 when every head keeps k; with head_keep (R22: head h keeps
+    head_keep[h] per row) values is [B][cap * sum(head_keep)] u16 and the region of (b, h)
+    starts at cap * sum(head_keep[:h]) within row b."""
 
-    def __init__(self, B, H, cap, d, k):
+    def __init__(self, B, H, cap, d, k, head_keep=None):
         self.B, self.H, self.cap, self.d, self.k = B, H, cap, d, k
+        self.head_keep = None
         self.bitmaps = np.zeros((B, H, cap, d // 64), dtype=np.uint64)
-        self.values = np.zeros((B, H, cap * k), dtype=np.uint16)
+        if head_keep is None:
+            self.values = np.zeros((B, H, cap * k), dtype=np.uint16)
+        else:
+            hk = np.ascontiguousarray(np.asarray(head_keep, dtype=np.int32))
+            assert hk.shape == (H,)
+            self.head_keep = hk
+            self.values = np.zeros((B, cap * int(hk.sum())), dtype=np.uint16)
         self.tile_off = np.zeros((B, H, cap // 64 + 1), dtype=np.uint32)
 
+    def _hk(self):
+        return None if self.head_keep is None else _p(self.head_keep)
 
-def compress(dense, seq_lens, k: int, cap: int | None = None, nthreads: int = 0) -> Compressed:
-    """dense: [B][H][T][d] fp16 -> Compressed (rows >= seq_lens[b] left zero)."""
+
+def compress(dense, seq_lens, k: int, cap: int | None = None, nthreads: int = 0,
+             head_keep=None) -> Compressed:
+    """dense: [B][H][T][d] fp16 -> Compressed (rows >= seq_lens[b] left zero).  With
+    head_keep, head h keeps head_keep[h] channels per row (k is then ignored by the rule)."""
     x = _u16(dense)
     B, H, T, d = x.shape
     cap = T if cap is None else cap
     cap = (cap + 63) // 64 * 64
     seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
-    c = Compressed(B, H, cap, d, k)
-    rc = lib().orc_compress(_p(x), B, H, T, d, _p(seq), int(k), cap, _p(c.bitmaps), _p(c.values),
-                            _p(c.tile_off), int(nthreads))
+    c = Compressed(B, H, cap, d, k, head_keep)
+    rc = lib().orc_compress_hk(_p(x), B, H, T, d, _p(seq), int(k), c._hk(), cap, _p(c.bitmaps),
+                               _p(c.values), _p(c.tile_off), int(nthreads))
     if rc != 0:
         raise ValueError("orc_compress: bad arguments")
     return c
@@ -135,16 +159,19 @@ def compress(dense, seq_lens, k: int, cap: int | None = None, nthreads: int = 0)
 def decompress(c: Compressed, seq_lens) -> np.ndarray:
     seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
     out = np.empty((c.B, c.H, c.cap, c.d), dtype=np.uint16)
-    rc = lib().orc_decompress(_p(c.bitmaps), _p(c.values), _p(c.tile_off), c.B, c.H, c.cap, c.d,
-                              c.k, _p(seq), _p(out))
+    rc = lib().orc_decompress_hk(_p(c.bitmaps), _p(c.values), _p(c.tile_off), c.B, c.H, c.cap,
+                                 c.d, c.k, c._hk(), _p(seq), _p(out))
     if rc != 0:
         raise ValueError("orc_decompress: bad arguments")
     return out
 
 
-def used_bytes(B, H, seq_lens, cap, d, k) -> int:
+def used_bytes(B, H, seq_lens, cap, d, k, head_keep=None) -> int:
     seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
-    return int(lib().orc_used_bytes(B, H, _p(seq), cap, d, k))
+    if head_keep is None:
+        return int(lib().orc_used_bytes(B, H, _p(seq), cap, d, k))
+    hk = np.ascontiguousarray(np.asarray(head_keep, dtype=np.int32))
+    return int(lib().orc_used_bytes_hk(B, H, _p(seq), cap, d, k, _p(hk)))
 
 
 def attention_dense(q, K, V, seq_lens, scale: float, nthreads: int = 0) -> np.ndarray:
@@ -173,10 +200,11 @@ def attention_compressed(q, kc: Compressed, vc: Compressed, seq_lens, scale: flo
     else:
         u = np.ascontiguousarray(np.asarray(units, dtype=np.int64))
         up, n = _p(u), u.size
-    rc = lib().orc_attention_compressed(_p(qb), B, Hq, kc.H, d, _p(kc.bitmaps), _p(kc.values),
-                                        _p(kc.tile_off), kc.k, _p(vc.bitmaps), _p(vc.values),
-                                        _p(vc.tile_off), vc.k, kc.cap, _p(seq), float(scale), up, n,
-                                        _p(out), int(nthreads))
+    rc = lib().orc_attention_compressed_hk(_p(qb), B, Hq, kc.H, d, _p(kc.bitmaps),
+                                           _p(kc.values), _p(kc.tile_off), kc.k, kc._hk(),
+                                           _p(vc.bitmaps), _p(vc.values), _p(vc.tile_off), vc.k,
+                                           vc._hk(), kc.cap, _p(seq), float(scale), up, n, _p(out),
+                                           int(nthreads))
     if rc != 0:
         raise ValueError("orc_attention_compressed: bad arguments")
     return out

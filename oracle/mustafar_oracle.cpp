@@ -31,6 +31,10 @@
 //   R8 attention scale is passed in (1/sqrt(d) in the tests).
 //   R9 q head hq reads kv head floor(hq / (Hq / Hkv)).
 //   R14 an empty sequence gives an all-zero output.
+//   R22 per-head keep: kv head h keeps head_keep[h] channels per row; the
+//       values of (batch b, head h) start at element cap * (b * S + P_h),
+//       S = the sum of head_keep over the heads, P_h = the sum over heads
+//       before h (the uniform layout when every head keeps the same k).
 //
 // Parity status: every function here is pinned by the CPU tests (fp16
 // decoder: exhaustive against IEEE-754 binary16; prune: brute force over all
@@ -109,6 +113,28 @@ int hw_threads() {
   return n ? static_cast<int>(n) : 1;
 }
 
+// R22: survivors per row of each kv head and where each (b, h) value region
+// starts.  head_keep == nullptr means every head keeps k.
+struct Layout {
+  std::vector<int64_t> keep, before;
+  int64_t sum = 0, cap = 0;
+  int64_t region(int64_t b, int64_t h) const { return cap * (b * sum + before[h]); }
+};
+
+bool make_layout(int H, const int32_t* head_keep, int k, int d, int64_t cap, Layout* L) {
+  L->keep.assign(H, k);
+  L->before.assign(H, 0);
+  L->cap = cap;
+  L->sum = 0;
+  for (int h = 0; h < H; ++h) {
+    if (head_keep) L->keep[h] = head_keep[h];
+    if (L->keep[h] < 0 || L->keep[h] > d) return false;
+    L->before[h] = L->sum;
+    L->sum += L->keep[h];
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,26 +171,31 @@ void orc_prune_rows(const uint16_t* x, int64_t n, int d, int k, uint8_t* keep) {
 //                                    r < min(64 j, T_b) of that (b, h)
 // Rows r >= T_b = min(seq_lens[b], cap, t_stride) are not written; nor are
 // tile_off entries j > ceil(T_b / 64).  Returns 0, or -1 on bad arguments.
-int orc_compress(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
-                 const int32_t* seq_lens, int k, int64_t cap, uint64_t* bitmaps,
-                 uint16_t* values, uint32_t* tile_off, int nthreads) {
+// With head_keep (R22) head h keeps head_keep[h] per row and the values of
+// (b, h) start at Layout::region(b, h); values is then [B][cap * S].
+int orc_compress_hk(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
+                    const int32_t* seq_lens, int k, const int32_t* head_keep, int64_t cap,
+                    uint64_t* bitmaps, uint16_t* values, uint32_t* tile_off, int nthreads) {
   if (d <= 0 || d % 64 != 0 || k < 0 || k > d || cap <= 0 || cap % 64 != 0) return -1;
+  Layout L;
+  if (!make_layout(H, head_keep, k, d, cap, &L)) return -1;
   const int words = d / 64;
   const int64_t ntile_entries = cap / 64 + 1;
   if (nthreads <= 0) nthreads = hw_threads();
   parallel_for(static_cast<int64_t>(B) * H, nthreads, [&](int64_t u) {
-    const int64_t b = u / H;
+    const int64_t b = u / H, h = u % H;
     const int T = clamp_len(seq_lens[b], std::min<int64_t>(cap, t_stride));
     const uint16_t* src = dense + u * t_stride * d;
     uint64_t* bm = bitmaps + u * cap * words;
-    uint16_t* val = values + u * cap * k;
+    uint16_t* val = values + L.region(b, h);
     uint32_t* toff = tile_off + u * ntile_entries;
+    const int kh = static_cast<int>(L.keep[h]);
     std::vector<uint8_t> keep(d);
     uint32_t count = 0;
     for (int r = 0; r < T; ++r) {
       if (r % 64 == 0) toff[r / 64] = count;
       const uint16_t* x = src + static_cast<int64_t>(r) * d;
-      prune_row(x, d, k, keep.data());
+      prune_row(x, d, kh, keep.data());
       for (int w = 0; w < words; ++w) bm[static_cast<int64_t>(r) * words + w] = 0;
       for (int c = 0; c < d; ++c) {
         if (keep[c]) {
@@ -178,19 +209,28 @@ int orc_compress(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
   return 0;
 }
 
+int orc_compress(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
+                 const int32_t* seq_lens, int k, int64_t cap, uint64_t* bitmaps,
+                 uint16_t* values, uint32_t* tile_off, int nthreads) {
+  return orc_compress_hk(dense, B, H, t_stride, d, seq_lens, k, nullptr, cap, bitmaps, values,
+                         tile_off, nthreads);
+}
+
 // Decompress (R7): walk the bitmap; a set bit takes the next stored value, a
 // clear bit gives +0.0.  Output [B][H][cap][d] fp16 bits; rows >= T_b are zero.
-int orc_decompress(const uint64_t* bitmaps, const uint16_t* values, const uint32_t* tile_off,
-                   int B, int H, int64_t cap, int d, int k, const int32_t* seq_lens,
-                   uint16_t* out) {
+int orc_decompress_hk(const uint64_t* bitmaps, const uint16_t* values, const uint32_t* tile_off,
+                      int B, int H, int64_t cap, int d, int k, const int32_t* head_keep,
+                      const int32_t* seq_lens, uint16_t* out) {
   if (d <= 0 || d % 64 != 0 || cap <= 0 || cap % 64 != 0) return -1;
+  Layout L;
+  if (!make_layout(H, head_keep, k, d, cap, &L)) return -1;
   const int words = d / 64;
   const int64_t ntile_entries = cap / 64 + 1;
   for (int64_t u = 0; u < static_cast<int64_t>(B) * H; ++u) {
-    const int64_t b = u / H;
+    const int64_t b = u / H, h = u % H;
     const int T = clamp_len(seq_lens[b], cap);
     const uint64_t* bm = bitmaps + u * cap * words;
-    const uint16_t* val = values + u * cap * k;
+    const uint16_t* val = values + L.region(b, h);
     const uint32_t* toff = tile_off + u * ntile_entries;
     uint16_t* dst = out + u * cap * d;
     std::memset(dst, 0, sizeof(uint16_t) * cap * d);
@@ -207,16 +247,31 @@ int orc_decompress(const uint64_t* bitmaps, const uint16_t* values, const uint32
   return 0;
 }
 
+int orc_decompress(const uint64_t* bitmaps, const uint16_t* values, const uint32_t* tile_off,
+                   int B, int H, int64_t cap, int d, int k, const int32_t* seq_lens,
+                   uint16_t* out) {
+  return orc_decompress_hk(bitmaps, values, tile_off, B, H, cap, d, k, nullptr, seq_lens, out);
+}
+
 // Bytes a compressed tensor occupies for the given lengths: per (b, h),
 // bitmaps (d/8 bytes per row) + kept values (2 bytes each) + tile offsets
 // (4 bytes per tile entry, ceil(T/64) + 1 entries).
-int64_t orc_used_bytes(int B, int H, const int32_t* seq_lens, int64_t cap, int d, int k) {
+// With head_keep, head h counts 2 * head_keep[h] bytes of values per row.
+int64_t orc_used_bytes_hk(int B, int H, const int32_t* seq_lens, int64_t cap, int d, int k,
+                          const int32_t* head_keep) {
   int64_t total = 0;
   for (int b = 0; b < B; ++b) {
     const int64_t T = clamp_len(seq_lens[b], cap);
-    total += static_cast<int64_t>(H) * (T * (d / 8) + 2 * T * k + 4 * ((T + 63) / 64 + 1));
+    for (int h = 0; h < H; ++h) {
+      const int64_t kh = head_keep ? head_keep[h] : k;
+      total += T * (d / 8) + 2 * T * kh + 4 * ((T + 63) / 64 + 1);
+    }
   }
   return total;
+}
+
+int64_t orc_used_bytes(int B, int H, const int32_t* seq_lens, int64_t cap, int d, int k) {
+  return orc_used_bytes_hk(B, H, seq_lens, cap, d, k, nullptr);
 }
 
 // Decode-step attention, the plain definition, fp64 ([Summary] "Approach":
@@ -266,22 +321,28 @@ int orc_attention_dense(const uint16_t* q, int B, int Hq, int Hkv, int d, const 
 // definition above is applied.  Only the (b, hq) pairs listed in `units`
 // (n_units entries of b*Hq + hq; all pairs when units == nullptr) are computed
 // and written to out[b][hq][:].  kk and kv are the survivor counts of K and V.
-int orc_attention_compressed(const uint16_t* q, int B, int Hq, int Hkv, int d,
-                             const uint64_t* kbm, const uint16_t* kval, const uint32_t* ktoff,
-                             int kk, const uint64_t* vbm, const uint16_t* vval,
-                             const uint32_t* vtoff, int kvk, int64_t cap,
-                             const int32_t* seq_lens, double scale, const int64_t* units,
-                             int64_t n_units, double* out, int nthreads) {
+// With kheads / vheads (R22) the value regions follow the per-head layout.
+int orc_attention_compressed_hk(const uint16_t* q, int B, int Hq, int Hkv, int d,
+                                const uint64_t* kbm, const uint16_t* kval, const uint32_t* ktoff,
+                                int kk, const int32_t* kheads, const uint64_t* vbm,
+                                const uint16_t* vval, const uint32_t* vtoff, int kvk,
+                                const int32_t* vheads, int64_t cap, const int32_t* seq_lens,
+                                double scale, const int64_t* units, int64_t n_units, double* out,
+                                int nthreads) {
   if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || d % 64 != 0 || cap % 64 != 0) return -1;
+  Layout KL, VL;
+  if (!make_layout(Hkv, kheads, kk, d, cap, &KL) || !make_layout(Hkv, vheads, kvk, d, cap, &VL))
+    return -1;
   const int G = Hq / Hkv;
   const int words = d / 64;
   const int64_t ntile_entries = cap / 64 + 1;
   if (nthreads <= 0) nthreads = hw_threads();
   const int64_t n = units ? n_units : static_cast<int64_t>(B) * Hq;
-  auto decode_rows = [&](const uint64_t* bm, const uint16_t* val, const uint32_t* toff, int k,
-                         int64_t unit, int T, std::vector<double>& dst) {
+  auto decode_rows = [&](const uint64_t* bm, const uint16_t* val, const uint32_t* toff,
+                         const Layout& L, int64_t b, int64_t h, int T, std::vector<double>& dst) {
+    const int64_t unit = b * Hkv + h;
     const uint64_t* ub = bm + unit * cap * words;
-    const uint16_t* uv = val + unit * cap * k;
+    const uint16_t* uv = val + L.region(b, h);
     const uint32_t* ut = toff + unit * ntile_entries;
     dst.assign(static_cast<size_t>(T) * d, 0.0);
     for (int tile = 0; tile * 64 < T; ++tile) {
@@ -295,14 +356,13 @@ int orc_attention_compressed(const uint16_t* q, int B, int Hq, int Hkv, int d,
   parallel_for(n, nthreads, [&](int64_t i) {
     const int64_t u = units ? units[i] : i;
     const int64_t b = u / Hq, hq = u % Hq, h = hq / G;
-    const int64_t unit = b * Hkv + h;
     const int T = clamp_len(seq_lens[b], cap);
     double* o = out + u * d;
     for (int c = 0; c < d; ++c) o[c] = 0.0;
     if (T == 0) return;
     std::vector<double> Kd, Vd, qd(d), s(T);
-    decode_rows(kbm, kval, ktoff, kk, unit, T, Kd);
-    decode_rows(vbm, vval, vtoff, kvk, unit, T, Vd);
+    decode_rows(kbm, kval, ktoff, KL, b, h, T, Kd);
+    decode_rows(vbm, vval, vtoff, VL, b, h, T, Vd);
     for (int c = 0; c < d; ++c) qd[c] = half_to_double(q[u * d + c]);
     for (int t = 0; t < T; ++t) {
       double acc = 0.0;
@@ -319,6 +379,17 @@ int orc_attention_compressed(const uint16_t* q, int B, int Hq, int Hkv, int d,
     for (int c = 0; c < d; ++c) o[c] /= l;
   });
   return 0;
+}
+
+int orc_attention_compressed(const uint16_t* q, int B, int Hq, int Hkv, int d,
+                             const uint64_t* kbm, const uint16_t* kval, const uint32_t* ktoff,
+                             int kk, const uint64_t* vbm, const uint16_t* vval,
+                             const uint32_t* vtoff, int kvk, int64_t cap,
+                             const int32_t* seq_lens, double scale, const int64_t* units,
+                             int64_t n_units, double* out, int nthreads) {
+  return orc_attention_compressed_hk(q, B, Hq, Hkv, d, kbm, kval, ktoff, kk, nullptr, vbm, vval,
+                                     vtoff, kvk, nullptr, cap, seq_lens, scale, units, n_units,
+                                     out, nthreads);
 }
 
 }  // extern "C"

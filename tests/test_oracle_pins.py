@@ -308,3 +308,84 @@ def test_attention_worked_examples():
             assert abs(outc[int(ch)] - val) < 1e-15, case["name"]
         others = [c for c in range(128) if str(c) not in case["expected_value"]]
         assert not out[others].any()
+
+
+# ---------------------------------------------------------------- per-head keep (R22)
+HEAD_KEEP = [26, 50, 0, 128, 38, 37]
+
+
+def test_head_keep_layout_and_rule():
+    """Per-head compression against the uniform rule applied head by head: head h of the
+    per-head cache holds exactly what a uniform compression of that head's slice with
+    keep = head_keep[h] holds, and its values sit at cap * (b * S + sum(head_keep[:h]))."""
+    rng = np.random.default_rng(21)
+    B, H, T, d = 2, len(HEAD_KEEP), 140, 128
+    x = rng.standard_normal((B, H, T, d)).astype(np.float16).view(np.uint16)
+    x[..., 5] = x[..., 6]  # ties between channels 5 and 6
+    seq = np.array([140, 65], np.int32)
+    cap = 192
+    c = oracle.compress(x, seq, max(HEAD_KEEP), cap=cap, head_keep=HEAD_KEEP)
+    S = sum(HEAD_KEEP)
+    assert c.values.shape == (B, cap * S)
+    for h, kh in enumerate(HEAD_KEEP):
+        u = oracle.compress(np.ascontiguousarray(x[:, h:h + 1]), seq, kh, cap=cap)
+        pre = sum(HEAD_KEEP[:h])
+        for b in range(B):
+            T_b = int(seq[b])
+            assert np.array_equal(c.bitmaps[b, h, :T_b], u.bitmaps[b, 0, :T_b])
+            ntile = (T_b + 63) // 64
+            assert np.array_equal(c.tile_off[b, h, :ntile + 1], u.tile_off[b, 0, :ntile + 1])
+            assert c.tile_off[b, h, :ntile + 1].tolist() == [min(64 * j, T_b) * kh
+                                                               for j in range(ntile + 1)]
+            start = cap * pre
+            assert np.array_equal(c.values[b, start:start + T_b * kh], u.values[b, 0, :T_b * kh])
+    # decompress: each head zero-masked by its own keep
+    dec = oracle.decompress(c, seq)
+    for h, kh in enumerate(HEAD_KEEP):
+        keep = oracle.prune_rows(x[:, h], kh)
+        for b in range(B):
+            T_b = int(seq[b])
+            expect = np.where(keep[b, :T_b] == 1, x[b, h, :T_b], 0).astype(np.uint16)
+            assert np.array_equal(dec[b, h, :T_b], expect)
+
+
+def test_head_keep_all_equal_is_the_uniform_layout():
+    rng = np.random.default_rng(22)
+    B, H, T = 2, 3, 100
+    x = rng.standard_normal((B, H, T, 128)).astype(np.float16).view(np.uint16)
+    seq = np.array([100, 37], np.int32)
+    a = oracle.compress(x, seq, 38, cap=128, head_keep=[38] * H)
+    u = oracle.compress(x, seq, 38, cap=128)
+    assert np.array_equal(a.values.reshape(u.values.shape), u.values)
+    assert np.array_equal(a.bitmaps, u.bitmaps) and np.array_equal(a.tile_off, u.tile_off)
+
+
+def test_head_keep_used_bytes_closed_form():
+    seq = np.array([100, 0, 64], np.int32)
+    hk = [10, 20, 30, 40]
+    exp = 0
+    for T in seq:
+        for k in hk:
+            exp += 16 * T + 2 * k * T + 4 * ((T + 63) // 64 + 1)
+    assert oracle.used_bytes(3, 4, seq, 128, 128, 40, head_keep=hk) == exp
+
+
+def test_head_keep_attention_equals_sdpa_on_zero_masked_cache():
+    rng = np.random.default_rng(23)
+    Hkv = len(HEAD_KEEP)
+    B, Hq, T = 2, 2 * Hkv, 130
+    q, K, V = _rand_inputs(rng, B, Hq, Hkv, T)
+    seq = np.array([130, 70], np.int32)
+    scale = 1.0 / math.sqrt(128)
+    vk = HEAD_KEEP[::-1]
+    kc = oracle.compress(K, seq, 128, head_keep=HEAD_KEEP)
+    vc = oracle.compress(V, seq, 128, head_keep=vk)
+    Km, Vm = oracle.decompress(kc, seq), oracle.decompress(vc, seq)
+    ref = _sdpa_f64(q, Km[:, :, :T], Vm[:, :, :T], seq, scale)
+    got = oracle.attention_compressed(q, kc, vc, seq, scale)
+    assert np.abs(got - ref).max() < 1e-12
+    # every head keeping all 128 channels is dense attention
+    kall = oracle.compress(K, seq, 128, head_keep=[128] * Hkv)
+    vall = oracle.compress(V, seq, 128, head_keep=[128] * Hkv)
+    dense = _sdpa_f64(q, K, V, seq, scale)
+    assert np.abs(oracle.attention_compressed(q, kall, vall, seq, scale) - dense).max() < 1e-12
