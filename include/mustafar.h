@@ -75,6 +75,16 @@ typedef enum {
  * capacity is the number of rows allocated per (batch, head): a positive
  * multiple of 64, at most 2^24, with capacity * keep * 2 < 2^31.  keep
  * (0..head_dim) is the number of survivors per row.  head_dim must be 128.
+ *
+ * Per-head keep (the per-head sparsity the [Summary] "Limitations" section
+ * leaves to future work): with head_keep set, kv head h keeps head_keep[h]
+ * values per row, keep must equal the largest entry, and values becomes
+ * uint16 [batch][capacity * S], S = the sum of head_keep, with the region of
+ * (b, h) starting at element capacity * (b * S + head_keep[0] + ... +
+ * head_keep[h - 1]); tile offsets count that head's values (min(64*j, T) *
+ * head_keep[h]).  With every head at the same keep this is the layout above.
+ * At most MUSTAFAR_MAX_HEAD_KEEP kv heads; entries outside 0..head_dim, or
+ * keep different from their maximum, return MUSTAFAR_EINVAL.
  * batch * num_kv_heads must stay below 2^31.  Calls that break these limits
  * return MUSTAFAR_EINVAL (MUSTAFAR_EUNSUPPORTED for another head_dim).
  * The decode calls also accept rows holding fewer than keep values (values
@@ -90,7 +100,11 @@ typedef struct {
   uint64_t *bitmaps;
   uint16_t *values;
   uint32_t *tile_offsets;
+  const int32_t *head_keep; /* (host) NULL, or num_kv_heads survivors per row, one per kv head;
+                               read during each call only */
 } mustafar_kv_t;
+
+#define MUSTAFAR_MAX_HEAD_KEEP 128 /* kv heads a per-head keep may describe */
 
 /* Text for a status code (static storage; never NULL). */
 const char *mustafar_status_str(int status);
@@ -115,7 +129,8 @@ int mustafar_kv_alloc_bytes(const mustafar_kv_t *kv, uint64_t *bitmaps_bytes,
 /*
  * Bytes the compressed tensor occupies for the given lengths (host array of
  * `batch` entries, clamped to [0, capacity]): per (batch, head) with T rows,
- * 16*T (bitmaps) + 2*keep*T (values) + 4*(ceil(T/64) + 1) (tile offsets).
+ * 16*T (bitmaps) + 2*keep*T (values; 2*head_keep[h]*T with per-head keep)
+ * + 4*(ceil(T/64) + 1) (tile offsets).
  * This is the compressed size compared with the dense 256*T bytes
  * ([Summary] "Key results" gives 45% of dense at 70% sparsity and 65% at 50%
  * for the authors' own layout).  Host only.

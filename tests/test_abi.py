@@ -190,3 +190,50 @@ def test_status_strings():
     for code in range(-5, 1):
         assert usk.status_str(code) not in ("", "unknown status")
     assert usk.status_str(-99) == "unknown status"
+
+
+def _kv_heads(head_keep, keep=None, batch=2, cap=128, ptrs=A16):
+    hk = np.ascontiguousarray(np.asarray(head_keep, dtype=np.int32))
+    k = int(hk.max()) if keep is None else keep
+    s = KV(batch, hk.size, 128, k, cap, ptrs, ptrs, ptrs, hk.ctypes.data)
+    s._hk = hk  # keep the host array alive with the struct
+    return s
+
+
+def test_head_keep_accounting_matches_oracle():
+    hk = [26, 50, 0, 128, 38, 37]
+    s = _kv_heads(hk, batch=3, cap=192, ptrs=None)
+    b, v, o = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    assert L.mustafar_kv_alloc_bytes(ctypes.byref(s), ctypes.byref(b), ctypes.byref(v),
+                                     ctypes.byref(o)) == 0
+    assert v.value == 3 * 192 * sum(hk) * 2 + 64
+    assert b.value == 3 * 6 * 192 * 16 and o.value == 3 * 6 * 4 * 4
+    seq = np.array([192, 0, 77], np.int32)
+    out = ctypes.c_int64()
+    assert L.mustafar_kv_used_bytes(ctypes.byref(s), seq.ctypes.data_as(ctypes.c_void_p),
+                                    ctypes.byref(out)) == 0
+    assert out.value == oracle.used_bytes(3, 6, seq, 192, 128, 128, head_keep=hk)
+    # every head at 38 takes the bytes of the uniform tensor
+    su = _kv_heads([38] * 6, batch=3, cap=192, ptrs=None)
+    assert L.mustafar_kv_alloc_bytes(ctypes.byref(su), ctypes.byref(b), ctypes.byref(v),
+                                     ctypes.byref(o)) == 0
+    assert (b.value, v.value, o.value) == _alloc(3, 6, 38, 192)[1:]
+
+
+def test_head_keep_argument_errors():
+    f = L.mustafar_prune_compress
+    bad = [
+        _kv_heads([38, 40], keep=38),          # keep is not the largest entry
+        _kv_heads([38, 129], keep=129),        # entry above head_dim
+        _kv_heads([38, -1], keep=38),          # negative entry
+        _kv_heads([1] * 129, keep=1),          # more kv heads than a per-head keep may describe
+    ]
+    for s in bad:
+        assert f(ctypes.byref(s), A16, 128, A16, None) == usk.MUSTAFAR_EINVAL
+        b = ctypes.c_uint64()
+        assert L.mustafar_kv_alloc_bytes(ctypes.byref(s), ctypes.byref(b), ctypes.byref(b),
+                                         ctypes.byref(b)) == usk.MUSTAFAR_EINVAL
+    k = _kv_heads([38, 40])
+    v = _kv_heads([38, 40], keep=38)
+    assert L.mustafar_append_token(ctypes.byref(k), ctypes.byref(v), A16, A16, A16, None, None) == \
+        usk.MUSTAFAR_EINVAL

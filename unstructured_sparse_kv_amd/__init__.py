@@ -21,6 +21,7 @@ MUSTAFAR_ELAUNCH = -4
 MUSTAFAR_ENOSPACE = -5
 STATUS_APPEND_FULL = 1
 HEAD_DIM = 128
+MAX_HEAD_KEEP = 128
 
 # Every symbol include/mustafar.h declares.
 EXPORTS = (
@@ -37,6 +38,7 @@ class KVStruct(ctypes.Structure):
         ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("keep", ctypes.c_int32), ("capacity", ctypes.c_int32),
         ("bitmaps", ctypes.c_void_p), ("values", ctypes.c_void_p), ("tile_offsets", ctypes.c_void_p),
+        ("head_keep", ctypes.c_void_p),
     ]
 
 
@@ -121,11 +123,22 @@ def decode_auto_splits(batch: int, num_kv_heads: int, max_seq_len: int) -> int:
 
 
 class CompressedKV:
-    """One compressed tensor (key or value cache of one layer) in device memory."""
+    """One compressed tensor (key or value cache of one layer) in device memory.
 
-    def __init__(self, batch: int, num_kv_heads: int, keep: int, capacity: int, device="cuda"):
+    With head_keep (a sequence of num_kv_heads ints), kv head h keeps head_keep[h]
+    values per row and `keep` is their maximum (pass keep=None to take it)."""
+
+    def __init__(self, batch: int, num_kv_heads: int, keep, capacity: int, device="cuda",
+                 head_keep=None):
+        import numpy as np
         import torch
-        self.s = KVStruct(batch, num_kv_heads, HEAD_DIM, keep, capacity, None, None, None)
+        self.head_keep = None
+        if head_keep is not None:
+            self.head_keep = np.ascontiguousarray(np.asarray(head_keep, dtype=np.int32))
+            if keep is None:
+                keep = int(self.head_keep.max())
+        self.s = KVStruct(batch, num_kv_heads, HEAD_DIM, keep, capacity, None, None, None,
+                          None if self.head_keep is None else self.head_keep.ctypes.data)
         nb, nv, no = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
         _check("mustafar_kv_alloc_bytes", lib().mustafar_kv_alloc_bytes(
             ctypes.byref(self.s), ctypes.byref(nb), ctypes.byref(nv), ctypes.byref(no)))
@@ -150,10 +163,15 @@ class CompressedKV:
         return out.value
 
     def views(self):
-        """(bitmaps [B][H][cap][2] int64, values [B][H][cap*keep] int16, tile_offsets [B][H][cap/64+1] int32)."""
+        """(bitmaps [B][H][cap][2] int64, values, tile_offsets [B][H][cap/64+1] int32); values is
+        [B][H][cap*keep] int16, or [B][cap*sum(head_keep)] with per-head keep."""
         B, H, cap, k = self.batch, self.num_kv_heads, self.capacity, self.keep
-        return (self.bitmaps.view(B, H, cap, 2), self.values[:B * H * cap * k].view(B, H, cap * k),
-                self.tile_offsets.view(B, H, cap // 64 + 1))
+        if self.head_keep is None:
+            vals = self.values[:B * H * cap * k].view(B, H, cap * k)
+        else:
+            S = int(self.head_keep.sum())
+            vals = self.values[:B * cap * S].view(B, cap * S)
+        return (self.bitmaps.view(B, H, cap, 2), vals, self.tile_offsets.view(B, H, cap // 64 + 1))
 
 
 def prune_compress(dst: CompressedKV, dense, seq_lens, stream=None) -> None:

@@ -17,7 +17,34 @@ constexpr int64_t kMaxCapacity = 1 << 24;
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
-int check_kv_shape(const mustafar_kv_t* kv) {
+// Survivors per row of each kv head: head_keep[h] when the caller gives
+// per-head keeps (keep must then be their maximum), else keep for every head.
+int make_keep_map(const mustafar_kv_t* kv, KeepMap* m) {
+  memset(m, 0, sizeof(*m));
+  m->keep = kv->keep;
+  if (!kv->head_keep) {
+    const int64_t sum = (int64_t)kv->num_kv_heads * kv->keep;
+    if (sum > INT32_MAX) return MUSTAFAR_EINVAL;
+    m->sum = (int32_t)sum;
+    return MUSTAFAR_OK;
+  }
+  if (kv->num_kv_heads > MUSTAFAR_MAX_HEAD_KEEP) return MUSTAFAR_EINVAL;
+  int most = 0, sum = 0;
+  for (int h = 0; h < kv->num_kv_heads; ++h) {
+    const int k = kv->head_keep[h];
+    if (k < 0 || k > kv->head_dim) return MUSTAFAR_EINVAL;
+    m->head[h] = (uint8_t)k;
+    m->before[h] = (uint16_t)sum;
+    sum += k;
+    most = k > most ? k : most;
+  }
+  if (most != kv->keep) return MUSTAFAR_EINVAL;
+  m->per_head = 1;
+  m->sum = sum;
+  return MUSTAFAR_OK;
+}
+
+int check_kv_shape(const mustafar_kv_t* kv, KeepMap* map_out = nullptr) {
   if (!kv) return MUSTAFAR_EINVAL;
   if (kv->batch <= 0 || kv->num_kv_heads <= 0) return MUSTAFAR_EINVAL;
   if ((int64_t)kv->batch * kv->num_kv_heads > INT32_MAX) return MUSTAFAR_EINVAL;  // unit index is 32-bit
@@ -28,11 +55,15 @@ int check_kv_shape(const mustafar_kv_t* kv) {
     return MUSTAFAR_EINVAL;
   // per-(batch, head) value region must be addressable with 32-bit byte offsets
   if ((int64_t)kv->capacity * kv->keep * 2 >= (int64_t)1 << 31) return MUSTAFAR_EINVAL;
+  KeepMap m;
+  const int rc = make_keep_map(kv, &m);
+  if (rc) return rc;
+  if (map_out) *map_out = m;
   return MUSTAFAR_OK;
 }
 
-int check_kv(const mustafar_kv_t* kv) {
-  int rc = check_kv_shape(kv);
+int check_kv(const mustafar_kv_t* kv, KeepMap* map_out = nullptr) {
+  int rc = check_kv_shape(kv, map_out);
   if (rc) return rc;
   if (!kv->bitmaps || !kv->values || !kv->tile_offsets) return MUSTAFAR_EINVAL;
   if (!aligned16(kv->bitmaps) || !aligned16(kv->values) || !aligned4(kv->tile_offsets))
@@ -98,9 +129,10 @@ int sparse_decode(SparseLauncher launch, const uint16_t* q, int32_t num_q_heads,
                   void* workspace, uint64_t workspace_bytes, void* stream,
                   const uint16_t* k_new = nullptr, const uint16_t* v_new = nullptr,
                   uint32_t* status = nullptr) {
-  int rc = check_kv(k);
+  SparseDecodeArgs a;
+  int rc = check_kv(k, &a.kmap);
   if (rc) return rc;
-  if ((rc = check_kv(v))) return rc;
+  if ((rc = check_kv(v, &a.vmap))) return rc;
   if (k->batch != v->batch || k->num_kv_heads != v->num_kv_heads || k->capacity != v->capacity)
     return MUSTAFAR_EINVAL;
   int sp = 0;
@@ -108,7 +140,6 @@ int sparse_decode(SparseLauncher launch, const uint16_t* q, int32_t num_q_heads,
                             out, workspace, workspace_bytes, seq_lens, &sp);
   if (rc) return rc;
   if ((rc = check_device())) return rc;
-  SparseDecodeArgs a;
   a.q = q;
   a.Hq = num_q_heads;
   a.Hkv = k->num_kv_heads;
@@ -160,26 +191,28 @@ int mustafar_keep_from_sparsity(double sparsity, int32_t head_dim) {
 
 int mustafar_kv_alloc_bytes(const mustafar_kv_t* kv, uint64_t* bitmaps_bytes,
                             uint64_t* values_bytes, uint64_t* offsets_bytes) {
-  const int rc = check_kv_shape(kv);
+  KeepMap m;
+  const int rc = check_kv_shape(kv, &m);
   if (rc) return rc;
   if (!bitmaps_bytes || !values_bytes || !offsets_bytes) return MUSTAFAR_EINVAL;
   const uint64_t units = (uint64_t)kv->batch * kv->num_kv_heads;
   *bitmaps_bytes = units * kv->capacity * (kv->head_dim / 64) * 8;
-  *values_bytes = units * kv->capacity * kv->keep * 2 + 64;
+  *values_bytes = (uint64_t)kv->batch * kv->capacity * (uint64_t)m.sum * 2 + 64;
   *offsets_bytes = units * (kv->capacity / 64 + 1) * 4;
   return MUSTAFAR_OK;
 }
 
 int mustafar_kv_used_bytes(const mustafar_kv_t* kv, const int32_t* seq_lens_host, int64_t* bytes) {
-  const int rc = check_kv_shape(kv);
+  KeepMap m;
+  const int rc = check_kv_shape(kv, &m);
   if (rc) return rc;
   if (!seq_lens_host || !bytes) return MUSTAFAR_EINVAL;
   int64_t total = 0;
   for (int b = 0; b < kv->batch; ++b) {
     int64_t T = seq_lens_host[b];
     T = T < 0 ? 0 : (T > kv->capacity ? kv->capacity : T);
-    total += (int64_t)kv->num_kv_heads *
-             (T * (kv->head_dim / 8) + 2 * T * kv->keep + 4 * ((T + 63) / 64 + 1));
+    total += (int64_t)kv->num_kv_heads * (T * (kv->head_dim / 8) + 4 * ((T + 63) / 64 + 1)) +
+             2 * T * (int64_t)m.sum;
   }
   *bytes = total;
   return MUSTAFAR_OK;
@@ -187,20 +220,22 @@ int mustafar_kv_used_bytes(const mustafar_kv_t* kv, const int32_t* seq_lens_host
 
 int mustafar_prune_compress(const mustafar_kv_t* dst, const uint16_t* dense, int64_t t_stride,
                             const int32_t* seq_lens, void* stream) {
-  int rc = check_kv(dst);
+  KeepMap m;
+  int rc = check_kv(dst, &m);
   if (rc) return rc;
   if (!dense || !seq_lens || !aligned16(dense) || !aligned4(seq_lens)) return MUSTAFAR_EINVAL;
   if (t_stride <= 0 || t_stride > kMaxCapacity * 64) return MUSTAFAR_EINVAL;
   if ((rc = check_device())) return rc;
-  return launched(launch_prune_compress(*dst, dense, t_stride, seq_lens, (hipStream_t)stream));
+  return launched(launch_prune_compress(*dst, m, dense, t_stride, seq_lens, (hipStream_t)stream));
 }
 
 int mustafar_append_token(const mustafar_kv_t* k, const mustafar_kv_t* v, const uint16_t* k_new,
                           const uint16_t* v_new, int32_t* seq_lens, uint32_t* status,
                           void* stream) {
-  int rc = check_kv(k);
+  KeepMap km, vm;
+  int rc = check_kv(k, &km);
   if (rc) return rc;
-  if ((rc = check_kv(v))) return rc;
+  if ((rc = check_kv(v, &vm))) return rc;
   if (k->batch != v->batch || k->num_kv_heads != v->num_kv_heads || k->capacity != v->capacity)
     return MUSTAFAR_EINVAL;
   if (!k_new || !v_new || !seq_lens) return MUSTAFAR_EINVAL;
@@ -208,7 +243,7 @@ int mustafar_append_token(const mustafar_kv_t* k, const mustafar_kv_t* v, const 
   if (status && !aligned4(status)) return MUSTAFAR_EINVAL;
   if (k->batch > 65535) return MUSTAFAR_EINVAL;
   if ((rc = check_device())) return rc;
-  return launched(launch_append(*k, *v, k_new, v_new, seq_lens, status, (hipStream_t)stream));
+  return launched(launch_append(*k, km, *v, vm, k_new, v_new, seq_lens, status, (hipStream_t)stream));
 }
 
 int mustafar_decode_auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len) {

@@ -93,9 +93,13 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
   const int tpw = (ntiles + total_waves - 1) / total_waves;
   const int tb = min(wid * tpw, ntiles), te = min(tb + tpw, ntiles);
 
-  const int kk = a.kk, vk = a.vk;
-  const auto krs = make_rsrc(a.kval + (int64_t)unit * a.cap * kk, (uint32_t)a.cap * kk * 2u);
-  const auto vrs = make_rsrc(a.vval + (int64_t)unit * a.cap * vk, (uint32_t)a.cap * vk * 2u);
+  constexpr uint32_t kKMapAt = offsetof(SparseDecodeArgs, kmap);
+  constexpr uint32_t kVMapAt = offsetof(SparseDecodeArgs, vmap);
+  const int kk = keep_of(a.kmap, kKMapAt, h), vk = keep_of(a.vmap, kVMapAt, h);
+  const int64_t kreg = region_of(a.kmap, kKMapAt, b, h, a.cap);
+  const int64_t vreg = region_of(a.vmap, kVMapAt, b, h, a.cap);
+  const auto krs = make_rsrc(a.kval + kreg, (uint32_t)a.cap * kk * 2u);
+  const auto vrs = make_rsrc(a.vval + vreg, (uint32_t)a.cap * vk * 2u);
   const auto kbrs = make_rsrc(a.kbm + (int64_t)unit * a.cap * 2, (uint32_t)a.cap * 16u);
   const auto vbrs = make_rsrc(a.vbm + (int64_t)unit * a.cap * 2, (uint32_t)a.cap * 16u);
   const auto ktrs = make_rsrc(a.ktoff + (int64_t)unit * ntoff, (uint32_t)ntoff * 4u);
@@ -256,11 +260,13 @@ hipError_t launch_sparse_t(const SparseDecodeArgs& a, int batch, hipStream_t str
 }
 
 // Straight-line kernels for the keeps of 70% and 50% sparsity at head_dim 128
-// (38 and 64); bucketed kernels for any other keep.
+// (38 and 64) when every head keeps the same; bucketed kernels for any other
+// keep and for per-head keeps.
 template <int G>
 hipError_t launch_sparse_g(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
-  if (a.kk == a.vk && a.kk == 38) return launch_sparse_t<G, 40, 38>(a, batch, stream);
-  if (a.kk == a.vk && a.kk == 64) return launch_sparse_t<G, 64, 64>(a, batch, stream);
+  const bool uniform = !a.kmap.per_head && !a.vmap.per_head;
+  if (uniform && a.kk == a.vk && a.kk == 38) return launch_sparse_t<G, 40, 38>(a, batch, stream);
+  if (uniform && a.kk == a.vk && a.kk == 64) return launch_sparse_t<G, 64, 64>(a, batch, stream);
   const int kmax = a.kk > a.vk ? a.kk : a.vk;
   if (kmax <= 32) return launch_sparse_t<G, 32, 0>(a, batch, stream);
   if (kmax <= 48) return launch_sparse_t<G, 48, 0>(a, batch, stream);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <stddef.h>
+
 #include <atomic>
 
 #include "../../include/mustafar.h"
@@ -14,9 +16,51 @@ constexpr int kDecodeWaves = 4;        // waves per decode block
 constexpr int kDecodeBlock = kDecodeWaves * 64;
 constexpr int kPartStride = 132;       // floats per (unit, split, q head) partial: m, l, acc[128], pad
 
+// Survivors per row of each kv head of one compressed tensor, and where the
+// value region of (batch b, head h) starts: element cap * (b * sum + before(h)),
+// which is unit * cap * keep when every head keeps `keep`.
+struct KeepMap {
+  int32_t keep;      // every head's keep, or the largest with per_head
+  int32_t per_head;  // the tables hold each head's keep and prefix
+  int32_t sum;       // keep summed over the kv heads
+  uint8_t head[MUSTAFAR_MAX_HEAD_KEEP];     // keep of head h
+  uint16_t before[MUSTAFAR_MAX_HEAD_KEEP];  // keep summed over heads 0 .. h-1
+};
+
+// A kernel reads its KeepMap tables through the kernel-argument segment
+// pointer: indexing the by-value argument with a run-time head index would make
+// the compiler copy the whole argument to scratch memory.  Every kernel that
+// takes a KeepMap has one argument, a struct, which the code-object ABI places
+// at offset 0 of the segment; `at` is the KeepMap's offset in that struct.
+// h must be uniform across the wave (the loads are scalar).
+typedef __attribute__((address_space(4))) const uint8_t kernarg_u8;
+typedef __attribute__((address_space(4))) const uint32_t kernarg_u32;
+
+// The aligned dword holding byte `at` of the kernel's argument struct, shifted
+// so that byte `at` is its low byte; `at` is uniform, and so is the result.
+__device__ __forceinline__ uint32_t kernarg_bytes_at(uint32_t at) {
+  kernarg_u8* seg = (kernarg_u8*)__builtin_amdgcn_kernarg_segment_ptr();
+  const uint32_t w = *reinterpret_cast<kernarg_u32*>(seg + (at & ~3u));
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(w >> (8u * (at & 3u))));
+}
+
+__device__ __forceinline__ int keep_of(const KeepMap& m, uint32_t at, int h) {
+  if (!m.per_head) return m.keep;
+  return (int)(kernarg_bytes_at(at + (uint32_t)offsetof(KeepMap, head) + (uint32_t)h) & 0xFFu);
+}
+
+__device__ __forceinline__ int64_t region_of(const KeepMap& m, uint32_t at, int64_t b, int h,
+                                             int cap) {
+  int64_t pre = (int64_t)h * m.keep;
+  if (m.per_head)
+    pre = kernarg_bytes_at(at + (uint32_t)offsetof(KeepMap, before) + 2u * (uint32_t)h) & 0xFFFFu;
+  return (int64_t)cap * (b * m.sum + pre);
+}
+
 struct SparseDecodeArgs {
   const uint16_t* q;
-  int32_t Hq, Hkv, cap, kk, vk, splits;
+  int32_t Hq, Hkv, cap, kk, vk, splits;  // kk, vk: the largest keep of K and V
+  KeepMap kmap, vmap;
   const uint64_t* kbm;
   const uint16_t* kval;
   const uint32_t* ktoff;
@@ -31,6 +75,32 @@ struct SparseDecodeArgs {
   // which then covers that row too (matrix-core kernel only)
   const uint16_t* k_new;
   const uint16_t* v_new;
+};
+
+struct PruneArgs {
+  const uint16_t* dense;
+  int64_t t_stride;
+  const int32_t* seq_lens;
+  int32_t H, cap, rows_per_unit, units;
+  uint64_t* bitmaps;
+  uint16_t* values;
+  uint32_t* tile_off;
+  KeepMap map;
+};
+
+struct AppendArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int32_t* seq_lens;
+  uint32_t* status;
+  int32_t H, cap;
+  uint64_t* kbm;
+  uint16_t* kval;
+  uint32_t* ktoff;
+  uint64_t* vbm;
+  uint16_t* vval;
+  uint32_t* vtoff;
+  KeepMap kmap, vmap;
 };
 
 struct DenseDecodeArgs {
@@ -65,11 +135,11 @@ inline uint64_t workspace_partial_bytes(int64_t batch, int64_t hq, int64_t split
   return (uint64_t)(batch * hq * splits * kPartStride * 4);
 }
 
-hipError_t launch_prune_compress(const mustafar_kv_t& dst, const uint16_t* dense, int64_t t_stride,
-                                 const int32_t* seq_lens, hipStream_t stream);
-hipError_t launch_append(const mustafar_kv_t& k, const mustafar_kv_t& v, const uint16_t* k_new,
-                         const uint16_t* v_new, int32_t* seq_lens, uint32_t* status,
-                         hipStream_t stream);
+hipError_t launch_prune_compress(const mustafar_kv_t& dst, const KeepMap& map, const uint16_t* dense,
+                                 int64_t t_stride, const int32_t* seq_lens, hipStream_t stream);
+hipError_t launch_append(const mustafar_kv_t& k, const KeepMap& kmap, const mustafar_kv_t& v,
+                         const KeepMap& vmap, const uint16_t* k_new, const uint16_t* v_new,
+                         int32_t* seq_lens, uint32_t* status, hipStream_t stream);
 hipError_t launch_decode_sparse(const SparseDecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_decode_sparse_valu(const SparseDecodeArgs& a, int batch, hipStream_t stream);
 hipError_t launch_decode_dense(const DenseDecodeArgs& a, int batch, hipStream_t stream);
