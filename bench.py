@@ -385,6 +385,24 @@ def main() -> int:
     log(f"vector-unit sparse decode (mustafar_decode_attn_valu), after a 1 GiB read: "
         f"{valu_s * 1e6:.1f} us")
 
+    # ---- per-head keep: layer 0's dense caches pruned with a keep per kv head
+    # (mean 38, so the same bytes as the uniform layer); the bucketed walk runs
+    kheads = [28, 32, 34, 38, 38, 42, 44, 48]
+    vheads = kheads[::-1]
+    seq_h = torch.full((B,), T0, dtype=torch.int32, device=dev)
+    kch = usk.CompressedKV(B, Hkv, None, cap, dev, head_keep=kheads)
+    vch = usk.CompressedKV(B, Hkv, None, cap, dev, head_keep=vheads)
+    usk.prune_compress(kch, K0, seq_h)
+    usk.prune_compress(vch, V0, seq_h)
+    torch.cuda.synchronize()
+    hk_s = median(timed(lambda: usk.decode_attn(q_last, kch, vch, seq_h, cap, scale, out, ws), 10,
+                        before=lambda: usk.probe_stream_read(flush, sink)))
+    sh0 = np.full(B, T0, np.int32)
+    hk_bytes = kch.used_bytes(sh0) + vch.used_bytes(sh0)
+    log(f"per-head keep K {kheads} / V {vheads}: decode after a 1 GiB read {hk_s * 1e6:.1f} us "
+        f"({hk_bytes / hk_s / 1e9:.0f} GB/s, {hk_bytes} bytes)")
+    del kch, vch
+
     # ---- dense fp16 comparison kernel (layer 0's caches, unpruned), batch 8 and batch 6
     dense = {}
     if not args.no_dense:
@@ -485,6 +503,10 @@ def main() -> int:
             "prefill_gbs_moved": round((dense_bytes0 + comp_bytes0) / prefill_s / 1e9, 1),
             "parity_last_step": parity,
             "clock_ramp_decode_calls": ramp_calls,
+            "head_keep_k": kheads,
+            "head_keep_v": vheads,
+            "head_keep_decode_us_after_1gib_read": round(hk_s * 1e6, 2),
+            "head_keep_decode_gbs_after_1gib_read": round(hk_bytes / hk_s / 1e9, 1),
         },
     }
     if dense:

@@ -49,21 +49,45 @@ __device__ __forceinline__ uint32_t value_at(const uint32_t (&row)[KW], int i) {
 // dwords are non-zero (invalid lanes carry all-ones words and zero values), so
 // the next dword is never empty and no lane runs out before the last step.
 // With EXACT the count is the compile-time NMAX and the walk is straight-line
-// code the compiler can software-pipeline.
+// code the compiler can software-pipeline.  Otherwise the count n (uniform
+// across the wave) is taken in chunks of 8 steps: a chunk that n covers
+// entirely is straight-line code too, and only the chunk holding the end of
+// the row tests each step (rows of up to 64 values; longer ones test every
+// step).
 template <int NMAX, bool EXACT, uint32_t MUL, int KW, class F>
 __device__ __forceinline__ void walk_fast(const uint32_t (&row)[KW], uint4 w, int n, uint32_t base,
                                           F&& f) {
   uint32_t cur = w.x, n1 = w.y, n2 = w.z, n3 = w.w;
+  auto step = [&](int i) {
+    f(base + (uint32_t)__builtin_ctz(cur) * MUL, value_at(row, i));
+    cur &= cur - 1u;
+    const bool z = (cur == 0u);
+    cur = z ? n1 : cur;
+    n1 = z ? n2 : n1;
+    n2 = z ? n3 : n2;
+    base += z ? 32u * MUL : 0u;
+  };
+  if constexpr (EXACT) {
 #pragma unroll
-  for (int i = 0; i < NMAX; ++i) {
-    if (EXACT || i < n) {
-      f(base + (uint32_t)__builtin_ctz(cur) * MUL, value_at(row, i));
-      cur &= cur - 1u;
-      const bool z = (cur == 0u);
-      cur = z ? n1 : cur;
-      n1 = z ? n2 : n1;
-      n2 = z ? n3 : n2;
-      base += z ? 32u * MUL : 0u;
+    for (int i = 0; i < NMAX; ++i) step(i);
+  } else if constexpr (NMAX > 64) {  // long rows: chunked code would spill registers
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i)
+      if (i < n) step(i);
+  } else {
+    constexpr int kChunk = 8;
+#pragma unroll
+    for (int i0 = 0; i0 < NMAX; i0 += kChunk) {
+      if (i0 >= n) break;
+      if (i0 + kChunk <= n) {
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j)
+          if (i0 + j < NMAX) step(i0 + j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j)
+          if (i0 + j < NMAX && i0 + j < n) step(i0 + j);
+      }
     }
   }
 }
