@@ -65,6 +65,10 @@ def lib():
                                                ctypes.c_int, P, P, P, ctypes.c_int, P, P, P,
                                                ctypes.c_int, I64, P, F64, P, I64, P, ctypes.c_int]
         Ci = ctypes.c_int
+        L.orc_prune_rows_24.restype = Ci
+        L.orc_prune_rows_24.argtypes = [P, I64, Ci, P]
+        L.orc_compress_24.restype = Ci
+        L.orc_compress_24.argtypes = [P, Ci, Ci, I64, Ci, P, I64, P, P, P, Ci]
         L.orc_compress_hk.restype = Ci
         L.orc_compress_hk.argtypes = [P, Ci, Ci, I64, Ci, P, Ci, P, I64, P, P, P, Ci]
         L.orc_decompress_hk.restype = Ci
@@ -114,6 +118,31 @@ def prune_rows(x, k: int) -> np.ndarray:
     keep = np.zeros(x.shape, dtype=np.uint8)
     lib().orc_prune_rows(_p(x), x.size // d, d, int(k), _p(keep))
     return keep
+
+
+def prune_rows_24(x) -> np.ndarray:
+    """x: [..., d] fp16, d % 4 == 0 -> uint8 keep mask (2:4 rule, R23)."""
+    x = _u16(x)
+    d = x.shape[-1]
+    keep = np.zeros(x.shape, dtype=np.uint8)
+    if lib().orc_prune_rows_24(_p(x), x.size // d, d, _p(keep)) != 0:
+        raise ValueError("orc_prune_rows_24: bad arguments")
+    return keep
+
+
+def compress_24(dense, seq_lens, cap: int | None = None, nthreads: int = 0) -> "Compressed":
+    """2:4 compression (R23) into the bitmap format with keep = d / 2."""
+    x = _u16(dense)
+    B, H, T, d = x.shape
+    cap = T if cap is None else cap
+    cap = (cap + 63) // 64 * 64
+    seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    c = Compressed(B, H, cap, d, d // 2)
+    rc = lib().orc_compress_24(_p(x), B, H, T, d, _p(seq), cap, _p(c.bitmaps), _p(c.values),
+                               _p(c.tile_off), int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_compress_24: bad arguments")
+    return c
 
 
 class Compressed:

@@ -31,6 +31,9 @@
 //   R8 attention scale is passed in (1/sqrt(d) in the tests).
 //   R9 q head hq reads kv head floor(hq / (Hq / Hkv)).
 //   R14 an empty sequence gives an all-zero output.
+//   R23 2:4 comparator: channels 4j..4j+3 of a row form a group; the 2 of
+//       largest magnitude survive (ties to the lower channel), stored in the
+//       same bitmap format with keep = d / 2.
 //   R22 per-head keep: kv head h keeps head_keep[h] channels per row; the
 //       values of (batch b, head h) start at element cap * (b * S + P_h),
 //       S = the sum of head_keep over the heads, P_h = the sum over heads
@@ -85,6 +88,14 @@ void prune_row(const uint16_t* x, int d, int k, uint8_t* keep) {
                    [&](int a, int b) { return mag_key(x[a]) > mag_key(x[b]); });
   std::memset(keep, 0, d);
   for (int i = 0; i < k && i < d; ++i) keep[idx[i]] = 1;
+}
+
+// 2:4 semi-structured pruning of one row (R23), the structured baseline the
+// pages argue against ([Summary] "Approach"; [Abstract]): in every group of 4
+// consecutive channels keep the 2 of largest magnitude, ties to the lower
+// channel -- the per-token rule above applied to each group with k = 2.
+void prune_row_24(const uint16_t* x, int d, uint8_t* keep) {
+  for (int g = 0; g + 4 <= d; g += 4) prune_row(x + g, 4, 2, keep + g);
 }
 
 int clamp_len(int32_t t, int64_t cap) {
@@ -163,6 +174,13 @@ void orc_prune_rows(const uint16_t* x, int64_t n, int d, int k, uint8_t* keep) {
   for (int64_t r = 0; r < n; ++r) prune_row(x + r * d, d, k, keep + r * d);
 }
 
+// The same with the 2:4 rule (R23); d must be a multiple of 4.
+int orc_prune_rows_24(const uint16_t* x, int64_t n, int d, uint8_t* keep) {
+  if (d <= 0 || d % 4 != 0) return -1;
+  for (int64_t r = 0; r < n; ++r) prune_row_24(x + r * d, d, keep + r * d);
+  return 0;
+}
+
 // Compress a dense cache [B][H][t_stride][d] (fp16 bits) into the bitmap format
 // ([Summary] "Approach": a bitmap-based compressed format; [Abstract]):
 //   bitmaps  [B][H][cap][d/64] u64   bit j of word w <=> channel 64w+j kept (R5, R6)
@@ -173,9 +191,10 @@ void orc_prune_rows(const uint16_t* x, int64_t n, int d, int k, uint8_t* keep) {
 // tile_off entries j > ceil(T_b / 64).  Returns 0, or -1 on bad arguments.
 // With head_keep (R22) head h keeps head_keep[h] per row and the values of
 // (b, h) start at Layout::region(b, h); values is then [B][cap * S].
-int orc_compress_hk(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
-                    const int32_t* seq_lens, int k, const int32_t* head_keep, int64_t cap,
-                    uint64_t* bitmaps, uint16_t* values, uint32_t* tile_off, int nthreads) {
+static int compress_rule(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
+                         const int32_t* seq_lens, int k, const int32_t* head_keep, int64_t cap,
+                         uint64_t* bitmaps, uint16_t* values, uint32_t* tile_off, int nthreads,
+                         bool two_four) {
   if (d <= 0 || d % 64 != 0 || k < 0 || k > d || cap <= 0 || cap % 64 != 0) return -1;
   Layout L;
   if (!make_layout(H, head_keep, k, d, cap, &L)) return -1;
@@ -195,7 +214,10 @@ int orc_compress_hk(const uint16_t* dense, int B, int H, int64_t t_stride, int d
     for (int r = 0; r < T; ++r) {
       if (r % 64 == 0) toff[r / 64] = count;
       const uint16_t* x = src + static_cast<int64_t>(r) * d;
-      prune_row(x, d, kh, keep.data());
+      if (two_four)
+        prune_row_24(x, d, keep.data());
+      else
+        prune_row(x, d, kh, keep.data());
       for (int w = 0; w < words; ++w) bm[static_cast<int64_t>(r) * words + w] = 0;
       for (int c = 0; c < d; ++c) {
         if (keep[c]) {
@@ -209,11 +231,27 @@ int orc_compress_hk(const uint16_t* dense, int B, int H, int64_t t_stride, int d
   return 0;
 }
 
+int orc_compress_hk(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
+                    const int32_t* seq_lens, int k, const int32_t* head_keep, int64_t cap,
+                    uint64_t* bitmaps, uint16_t* values, uint32_t* tile_off, int nthreads) {
+  return compress_rule(dense, B, H, t_stride, d, seq_lens, k, head_keep, cap, bitmaps, values,
+                       tile_off, nthreads, false);
+}
+
 int orc_compress(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
                  const int32_t* seq_lens, int k, int64_t cap, uint64_t* bitmaps,
                  uint16_t* values, uint32_t* tile_off, int nthreads) {
   return orc_compress_hk(dense, B, H, t_stride, d, seq_lens, k, nullptr, cap, bitmaps, values,
                          tile_off, nthreads);
+}
+
+// 2:4 compression (R23) into the bitmap format with keep = d / 2: the layout
+// of orc_compress, every 4-channel group of every row holding 2 set bits.
+int orc_compress_24(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
+                    const int32_t* seq_lens, int64_t cap, uint64_t* bitmaps, uint16_t* values,
+                    uint32_t* tile_off, int nthreads) {
+  return compress_rule(dense, B, H, t_stride, d, seq_lens, d / 2, nullptr, cap, bitmaps, values,
+                       tile_off, nthreads, true);
 }
 
 // Decompress (R7): walk the bitmap; a set bit takes the next stored value, a

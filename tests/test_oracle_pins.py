@@ -389,3 +389,60 @@ def test_head_keep_attention_equals_sdpa_on_zero_masked_cache():
     vall = oracle.compress(V, seq, 128, head_keep=[128] * Hkv)
     dense = _sdpa_f64(q, K, V, seq, scale)
     assert np.abs(oracle.attention_compressed(q, kall, vall, seq, scale) - dense).max() < 1e-12
+
+
+# ---------------------------------------------------------------- 2:4 comparator rule (R23)
+def test_prune_24_matches_brute_force_per_group():
+    rng = np.random.default_rng(31)
+    alphabet = np.array([0x0000, 0x8000, 0x0001, 0x3C00, 0xBC00, 0x4000, 0xC000, 0x3800, 0x7BFF],
+                        dtype=np.uint16)
+    for trial in range(40):
+        row = alphabet[rng.integers(0, alphabet.size, size=(1, 128))]
+        keep = oracle.prune_rows_24(row)[0]
+        for g in range(32):
+            keys = row[0, 4 * g:4 * g + 4] & 0x7FFF
+            want = _brute_force_keep(keys, 2)
+            got = set(np.nonzero(keep[4 * g:4 * g + 4])[0].tolist())
+            assert got == want, (trial, g, keys)
+
+
+def test_prune_24_invariants_and_special_rows():
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((200, 128)).astype(np.float16).view(np.uint16)
+    keep = oracle.prune_rows_24(x)
+    kg = keep.reshape(200, 32, 4)
+    assert (kg.sum(-1) == 2).all()
+    key = (x & 0x7FFF).reshape(200, 32, 4).astype(np.int64)
+    kept_min = np.where(kg == 1, key, 1 << 20).min(-1)
+    pruned_max = np.where(kg == 0, key, -1).max(-1)
+    assert (kept_min >= pruned_max).all()
+    # two zeros and two non-zeros per group: the non-zeros survive, so nothing is lost
+    y = x.copy().reshape(200, 32, 4)
+    y[:, :, [0, 3]] = 0
+    y = y.reshape(200, 128)
+    c = oracle.compress_24(y.reshape(1, 1, 200, 128), [200], cap=256)
+    assert np.array_equal(oracle.decompress(c, [200])[0, 0, :200], y)
+
+
+def test_compress_24_layout_and_attention():
+    rng = np.random.default_rng(33)
+    B, Hq, Hkv, T = 2, 4, 2, 150
+    q, K, V = _rand_inputs(rng, B, Hq, Hkv, T)
+    seq = np.array([150, 70], np.int32)
+    kc, vc = oracle.compress_24(K, seq, cap=192), oracle.compress_24(V, seq, cap=192)
+    assert kc.k == 64 and kc.values.shape == (B, Hkv, 192 * 64)
+    keep = oracle.prune_rows_24(K)
+    for b in range(B):
+        T_b = int(seq[b])
+        for h in range(Hkv):
+            words = kc.bitmaps[b, h, :T_b]
+            nib = [(int(w) >> (4 * j)) & 0xF for w in words.reshape(-1) for j in range(16)]
+            assert all(bin(n).count("1") == 2 for n in nib)
+            flat = K[b, h, :T_b][keep[b, h, :T_b] == 1]
+            assert np.array_equal(kc.values[b, h, :T_b * 64], flat)
+            nt = (T_b + 63) // 64
+            assert kc.tile_off[b, h, :nt + 1].tolist() == [min(64 * j, T_b) * 64 for j in range(nt + 1)]
+    Km, Vm = oracle.decompress(kc, seq), oracle.decompress(vc, seq)
+    ref = _sdpa_f64(q, Km[:, :, :T], Vm[:, :, :T], seq, 1.0 / math.sqrt(128))
+    got = oracle.attention_compressed(q, kc, vc, seq, 1.0 / math.sqrt(128))
+    assert np.abs(got - ref).max() < 1e-12
