@@ -277,6 +277,34 @@ int mustafar_decode_step(const uint16_t *q, int32_t num_q_heads, const mustafar_
                          void *stream);
 
 /*
+ * 2:4 semi-structured comparator, prefill: prunes every row of `dense` so that
+ * each group of 4 consecutive channels keeps its 2 entries of largest
+ * magnitude (ties to the lower channel) and stores them in the bitmap format
+ * above.  2:4 semi-structured sparsity is one of the baselines the pages list
+ * ([Summary] "Experimental setup"); at 50% it stores exactly the bytes of
+ * unstructured pruning at keep 64, so the two formats can be compared at equal
+ * size.  dst->keep must be 64 (head_dim / 2) and dst->head_keep NULL, else
+ * MUSTAFAR_EINVAL.  Other arguments, layout and errors as
+ * mustafar_prune_compress.
+ */
+int mustafar_prune_compress_24(const mustafar_kv_t *dst, const uint16_t *dense, int64_t t_stride,
+                               const int32_t *seq_lens, void *stream);
+
+/*
+ * 2:4 comparator, decode: the attention of mustafar_decode_attn over key and
+ * value caches written by mustafar_prune_compress_24, computed with the
+ * structure (each group's two values expanded in registers; no bitmap walk).
+ * Both caches must have keep 64 and no head_keep (MUSTAFAR_EINVAL otherwise),
+ * and every stored row must hold exactly two values in each group of 4
+ * channels; for other contents the output is unspecified (mustafar_decode_attn
+ * reads any cache).  Arguments, workspace and errors as mustafar_decode_attn.
+ */
+int mustafar_decode_attn_24(const uint16_t *q, int32_t num_q_heads, const mustafar_kv_t *k,
+                            const mustafar_kv_t *v, const int32_t *seq_lens, int32_t max_seq_len,
+                            float scale, int32_t splits, uint16_t *out, void *workspace,
+                            uint64_t workspace_bytes, void *stream);
+
+/*
  * The same attention over dense, unpruned fp16 caches: the comparison
  * baseline (the pages compare against dense attention, [Summary] "Key results"
  * and "Experimental setup").  q.K^T runs on the matrix cores (MFMA), P.V and

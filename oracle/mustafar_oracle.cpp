@@ -90,8 +90,9 @@ void prune_row(const uint16_t* x, int d, int k, uint8_t* keep) {
   for (int i = 0; i < k && i < d; ++i) keep[idx[i]] = 1;
 }
 
-// 2:4 semi-structured pruning of one row (R23), the structured baseline the
-// pages argue against ([Summary] "Approach"; [Abstract]): in every group of 4
+// 2:4 semi-structured pruning of one row (R23), a baseline the pages list
+// ([Summary] "Experimental setup") and the structured kind of sparsity they
+// argue against ([Abstract]): in every group of 4
 // consecutive channels keep the 2 of largest magnitude, ties to the lower
 // channel -- the per-token rule above applied to each group with k = 2.
 void prune_row_24(const uint16_t* x, int d, uint8_t* keep) {

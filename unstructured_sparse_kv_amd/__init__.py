@@ -30,6 +30,7 @@ EXPORTS = (
     "mustafar_decode_auto_splits", "mustafar_decode_workspace_bytes",
     "mustafar_decode_workspace_init", "mustafar_decode_attn", "mustafar_decode_attn_valu",
     "mustafar_decode_step", "mustafar_dense_decode_attn", "mustafar_probe_stream_read",
+    "mustafar_prune_compress_24", "mustafar_decode_attn_24",
 )
 
 
@@ -84,6 +85,9 @@ def lib() -> ctypes.CDLL:
             "mustafar_dense_decode_attn": (ctypes.c_int, [P, I32, P, P, I32, I32, I32, I64, P, I32,
                                                           ctypes.c_float, I32, P, P, U64, P]),
             "mustafar_probe_stream_read": (ctypes.c_int, [P, U64, P, P]),
+            "mustafar_prune_compress_24": (ctypes.c_int, [KVP, P, I64, P, P]),
+            "mustafar_decode_attn_24": (ctypes.c_int, [P, I32, KVP, KVP, P, I32, ctypes.c_float, I32,
+                                                       P, P, U64, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -181,6 +185,13 @@ def prune_compress(dst: CompressedKV, dense, seq_lens, stream=None) -> None:
         dst.ref, dense.data_ptr(), dense.shape[2], seq_lens.data_ptr(), _stream(stream)))
 
 
+def prune_compress_24(dst: CompressedKV, dense, seq_lens, stream=None) -> None:
+    """2:4 comparator: dense [B][H][t_stride][128] fp16 -> dst (keep 64)."""
+    assert dense.is_contiguous() and dense.shape[-1] == HEAD_DIM
+    _check("mustafar_prune_compress_24", lib().mustafar_prune_compress_24(
+        dst.ref, dense.data_ptr(), dense.shape[2], seq_lens.data_ptr(), _stream(stream)))
+
+
 def append_token(k: CompressedKV, v: CompressedKV, k_new, v_new, seq_lens, status=None,
                  stream=None) -> None:
     """k_new / v_new: [B][H][128] fp16 (device); seq_lens int32 [B] advanced in place."""
@@ -222,6 +233,15 @@ def decode_attn_valu(q, k: CompressedKV, v: CompressedKV, seq_lens, max_seq_len:
     """Same as decode_attn, vector-unit kernel."""
     assert q.is_contiguous() and out.is_contiguous()
     _check("mustafar_decode_attn_valu", lib().mustafar_decode_attn_valu(
+        q.data_ptr(), q.shape[1], k.ref, v.ref, seq_lens.data_ptr(), max_seq_len, scale, splits,
+        out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def decode_attn_24(q, k: CompressedKV, v: CompressedKV, seq_lens, max_seq_len: int, scale: float,
+                   out, workspace, splits: int = 0, stream=None) -> None:
+    """Same as decode_attn over 2:4 caches (from prune_compress_24), 2:4 kernel."""
+    assert q.is_contiguous() and out.is_contiguous()
+    _check("mustafar_decode_attn_24", lib().mustafar_decode_attn_24(
         q.data_ptr(), q.shape[1], k.ref, v.ref, seq_lens.data_ptr(), max_seq_len, scale, splits,
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
 

@@ -9,8 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmustafar.so")
-SOURCES = ["api.hip", "prune.hip", "decode_sparse_mfma.hip", "decode_sparse.hip", "decode_dense.hip",
-           "util.hip"]
+SOURCES = ["api.hip", "prune.hip", "decode_sparse_mfma.hip", "decode_sparse.hip", "decode_24.hip",
+           "decode_dense.hip", "util.hip"]
 ARCH = os.environ.get("MUSTAFAR_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -23,6 +23,7 @@ FLAGS = [
 # that rescales them needs no copies to and from the accumulation registers.
 FILE_FLAGS = {
     "decode_sparse_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode_24.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "decode_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

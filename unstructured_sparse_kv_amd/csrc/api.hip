@@ -229,6 +229,19 @@ int mustafar_prune_compress(const mustafar_kv_t* dst, const uint16_t* dense, int
   return launched(launch_prune_compress(*dst, m, dense, t_stride, seq_lens, (hipStream_t)stream));
 }
 
+int mustafar_prune_compress_24(const mustafar_kv_t* dst, const uint16_t* dense, int64_t t_stride,
+                               const int32_t* seq_lens, void* stream) {
+  KeepMap m;
+  int rc = check_kv(dst, &m);
+  if (rc) return rc;
+  if (dst->keep != kHeadDim / 2 || dst->head_keep) return MUSTAFAR_EINVAL;
+  if (!dense || !seq_lens || !aligned16(dense) || !aligned4(seq_lens)) return MUSTAFAR_EINVAL;
+  if (t_stride <= 0 || t_stride > kMaxCapacity * 64) return MUSTAFAR_EINVAL;
+  if ((rc = check_device())) return rc;
+  return launched(
+      launch_prune_compress(*dst, m, dense, t_stride, seq_lens, (hipStream_t)stream, true));
+}
+
 int mustafar_append_token(const mustafar_kv_t* k, const mustafar_kv_t* v, const uint16_t* k_new,
                           const uint16_t* v_new, int32_t* seq_lens, uint32_t* status,
                           void* stream) {
@@ -285,6 +298,16 @@ int mustafar_decode_attn_valu(const uint16_t* q, int32_t num_q_heads, const must
                               uint64_t workspace_bytes, void* stream) {
   return sparse_decode(launch_decode_sparse_valu, q, num_q_heads, k, v, seq_lens, max_seq_len,
                        scale, splits, out, workspace, workspace_bytes, stream);
+}
+
+int mustafar_decode_attn_24(const uint16_t* q, int32_t num_q_heads, const mustafar_kv_t* k,
+                            const mustafar_kv_t* v, const int32_t* seq_lens, int32_t max_seq_len,
+                            float scale, int32_t splits, uint16_t* out, void* workspace,
+                            uint64_t workspace_bytes, void* stream) {
+  for (const mustafar_kv_t* c : {k, v})
+    if (c && (c->keep != kHeadDim / 2 || c->head_keep)) return MUSTAFAR_EINVAL;
+  return sparse_decode(launch_decode_24, q, num_q_heads, k, v, seq_lens, max_seq_len, scale,
+                       splits, out, workspace, workspace_bytes, stream);
 }
 
 int mustafar_decode_step(const uint16_t* q, int32_t num_q_heads, const mustafar_kv_t* k,

@@ -21,6 +21,9 @@ constexpr int kRowsPerWave = kTile / kWavesPerBlock;  // 16
 // the next row's loads in flight.  Units beyond gridDim.y are taken in steps
 // of gridDim.y.  Row indices stay 32-bit within a unit.  Head h of a unit keeps
 // keep_of(map, h) values per row.
+// TWO_FOUR: the 2:4 comparator rule instead of the per-token top-keep rule
+// (the map then holds keep = 64 for every head).
+template <bool TWO_FOUR>
 __global__ __launch_bounds__(kPruneBlock) void prune_compress_kernel(PruneArgs a) {
   constexpr uint32_t kMapAt = offsetof(PruneArgs, map);
   const uint32_t lane = lane_id();
@@ -45,7 +48,7 @@ __global__ __launch_bounds__(kPruneBlock) void prune_compress_kernel(PruneArgs a
       // next row's loads (the last row reloads itself)
       const int64_t step = (t + 1 < tend) ? kHeadDim : 0;
       const uint32_t y0 = src[step + lane], y1 = src[step + lane + 64];
-      const RowMask m = select_row(x0, x1, keep);
+      const RowMask m = TWO_FOUR ? select_row_24(x0, x1) : select_row(x0, x1, keep);
       store_row(m, x0, x1, bm, vals);
       if (lane == 0) {
         if (t % kTile == 0) toff[t / kTile] = (uint32_t)(t * keep);
@@ -105,7 +108,8 @@ __global__ __launch_bounds__(1024) void append_kernel(AppendArgs a) {
 }  // namespace
 
 hipError_t launch_prune_compress(const mustafar_kv_t& d, const KeepMap& map, const uint16_t* dense,
-                                 int64_t t_stride, const int32_t* seq_lens, hipStream_t stream) {
+                                 int64_t t_stride, const int32_t* seq_lens, hipStream_t stream,
+                                 bool two_four) {
   const int64_t rows_per_unit = t_stride < d.capacity ? t_stride : d.capacity;
   const int64_t units = (int64_t)d.batch * d.num_kv_heads;
   const int64_t tiles = (rows_per_unit + kTile - 1) / kTile;
@@ -123,8 +127,12 @@ hipError_t launch_prune_compress(const mustafar_kv_t& d, const KeepMap& map, con
   a.values = d.values;
   a.tile_off = d.tile_offsets;
   a.map = map;
-  hipLaunchKernelGGL(prune_compress_kernel, dim3((unsigned)tiles, gy), dim3(kPruneBlock), 0, stream,
-                     a);
+  if (two_four)
+    hipLaunchKernelGGL(prune_compress_kernel<true>, dim3((unsigned)tiles, gy), dim3(kPruneBlock), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(prune_compress_kernel<false>, dim3((unsigned)tiles, gy), dim3(kPruneBlock), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

@@ -41,6 +41,33 @@ __device__ __forceinline__ RowMask select_row(uint32_t x0, uint32_t x1, int keep
   return RowMask{__ballot(keep0), __ballot(keep1)};
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// The lane's channel survives the 2:4 rule: of the 4 lanes of its quad (one
+// group of 4 consecutive channels) the 2 of largest key survive, ties to the
+// lower channel.  A partner lane (lane ^ s) holds a lower channel exactly when
+// the highest bit of s is set in the lane's position within the quad.
+__device__ __forceinline__ bool keep_24(uint32_t k) {
+  const uint32_t me = lane_id() & 3u;
+  const uint32_t k1 = quad_mov<0xB1>(k);  // lane ^ 1
+  const uint32_t k2 = quad_mov<0x4E>(k);  // lane ^ 2
+  const uint32_t k3 = quad_mov<0x1B>(k);  // lane ^ 3
+  const int beaten = (int)(k1 > k || (k1 == k && (me & 1u))) +
+                     (int)(k2 > k || (k2 == k && (me & 2u))) +
+                     (int)(k3 > k || (k3 == k && (me & 2u)));
+  return beaten < 2;
+}
+
+// 2:4 semi-structured selection of one row (the structured comparator of the
+// unstructured rule above): 2 survivors in every group of 4 consecutive
+// channels, chosen by magnitude key with ties to the lower channel.
+__device__ __forceinline__ RowMask select_row_24(uint32_t x0, uint32_t x1) {
+  return RowMask{__ballot(keep_24(x0 & 0x7FFFu)), __ballot(keep_24(x1 & 0x7FFFu))};
+}
+
 // Writes the row's bitmap words and packs its kept values (ascending channel)
 // at `vals`.
 __device__ __forceinline__ void store_row(const RowMask& m, uint32_t x0, uint32_t x1,
