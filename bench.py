@@ -403,6 +403,40 @@ def main() -> int:
         f"({hk_bytes / hk_s / 1e9:.0f} GB/s, {hk_bytes} bytes)")
     del kch, vch
 
+    # ---- 2:4 comparator at 50%: layer 0's dense caches pruned 2:4 and pruned
+    # per token to keep 64 (the same bytes); the 2:4 kernel and the unstructured
+    # kernel on the 2:4 caches, the unstructured kernel on its own caches; each
+    # output's distance to the dense attention over the unpruned caches
+    k24 = usk.CompressedKV(B, Hkv, 64, cap, dev)
+    v24 = usk.CompressedKV(B, Hkv, 64, cap, dev)
+    usk.prune_compress_24(k24, K0, seq_h)
+    usk.prune_compress_24(v24, V0, seq_h)
+    k64 = usk.CompressedKV(B, Hkv, 64, cap, dev)
+    v64 = usk.CompressedKV(B, Hkv, 64, cap, dev)
+    usk.prune_compress(k64, K0, seq_h)
+    usk.prune_compress(v64, V0, seq_h)
+    torch.cuda.synchronize()
+    b50 = k24.used_bytes(sh0) + v24.used_bytes(sh0)
+    cmp50 = {}
+    outs50 = {}
+    for name, fn, kc_, vc_ in (("2:4 kernel, 2:4 caches", usk.decode_attn_24, k24, v24),
+                               ("unstructured kernel, 2:4 caches", usk.decode_attn, k24, v24),
+                               ("unstructured kernel, keep-64 caches", usk.decode_attn, k64, v64)):
+        t_ = median(timed(lambda: fn(q_last, kc_, vc_, seq_h, cap, scale, out, ws), 10,
+                          before=lambda: usk.probe_stream_read(flush, sink)))
+        outs50[name] = out.float().clone()
+        cmp50[name] = t_
+        log(f"50% sparsity, {name}: {t_ * 1e6:.1f} us ({b50 / t_ / 1e9:.0f} GB/s)")
+    wsd0 = usk.make_workspace(B, Hq, Hkv, T0)
+    outd0 = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+    usk.dense_decode_attn(q_last, K0, V0, seq_h, T0, scale, outd0, wsd0)
+    torch.cuda.synchronize()
+    ref_d = outd0.float()
+    err50 = {n: float(torch.linalg.norm(o - ref_d) / torch.linalg.norm(ref_d)) for n, o in outs50.items()}
+    for n, e in err50.items():
+        log(f"50% sparsity, {n}: relative L2 distance to dense attention {e:.4f}")
+    del k24, v24, k64, v64, wsd0
+
     # ---- dense fp16 comparison kernel (layer 0's caches, unpruned), batch 8 and batch 6
     dense = {}
     if not args.no_dense:
@@ -507,6 +541,9 @@ def main() -> int:
             "head_keep_v": vheads,
             "head_keep_decode_us_after_1gib_read": round(hk_s * 1e6, 2),
             "head_keep_decode_gbs_after_1gib_read": round(hk_bytes / hk_s / 1e9, 1),
+            "sparsity50_bytes": int(b50),
+            "sparsity50_us_after_1gib_read": {n: round(t_ * 1e6, 2) for n, t_ in cmp50.items()},
+            "sparsity50_rel_l2_to_dense": {n: round(e, 5) for n, e in err50.items()},
         },
     }
     if dense:
