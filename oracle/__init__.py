@@ -67,6 +67,8 @@ def lib():
         Ci = ctypes.c_int
         L.orc_prune_rows_24.restype = Ci
         L.orc_prune_rows_24.argtypes = [P, I64, Ci, P]
+        L.orc_compress_channel.restype = Ci
+        L.orc_compress_channel.argtypes = [P, Ci, Ci, I64, Ci, P, Ci, I64, P, P, P, Ci]
         L.orc_compress_24.restype = Ci
         L.orc_compress_24.argtypes = [P, Ci, Ci, I64, Ci, P, I64, P, P, P, Ci]
         L.orc_compress_hk.restype = Ci
@@ -142,6 +144,23 @@ def compress_24(dense, seq_lens, cap: int | None = None, nthreads: int = 0) -> "
                                _p(c.tile_off), int(nthreads))
     if rc != 0:
         raise ValueError("orc_compress_24: bad arguments")
+    return c
+
+
+def compress_channel(dense, seq_lens, keep: int, cap: int | None = None,
+                     nthreads: int = 0) -> "Compressed":
+    """Channel-wise pruning (R24) into the bitmap format: per full 64-row tile each channel
+    keeps keep/2 entries; a final partial tile is pruned per token to keep."""
+    x = _u16(dense)
+    B, H, T, d = x.shape
+    cap = T if cap is None else cap
+    cap = (cap + 63) // 64 * 64
+    seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    c = Compressed(B, H, cap, d, keep)
+    rc = lib().orc_compress_channel(_p(x), B, H, T, d, _p(seq), int(keep), cap, _p(c.bitmaps),
+                                    _p(c.values), _p(c.tile_off), int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_compress_channel: bad arguments")
     return c
 
 

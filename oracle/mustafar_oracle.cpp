@@ -34,6 +34,10 @@
 //   R23 2:4 comparator: channels 4j..4j+3 of a row form a group; the 2 of
 //       largest magnitude survive (ties to the lower channel), stored in the
 //       same bitmap format with keep = d / 2.
+//   R24 channel-wise pruning: in every full 64-row tile of a (b, h), each
+//       channel keeps its keep/2 entries of largest magnitude over the tile's
+//       rows (ties to the earlier row); rows of a final partial tile are pruned
+//       per token to keep.  Same bitmap format; rows hold 0..d values.
 //   R22 per-head keep: kv head h keeps head_keep[h] channels per row; the
 //       values of (batch b, head h) start at element cap * (b * S + P_h),
 //       S = the sum of head_keep over the heads, P_h = the sum over heads
@@ -190,6 +194,61 @@ int orc_prune_rows_24(const uint16_t* x, int64_t n, int d, uint8_t* keep) {
 //                                    r < min(64 j, T_b) of that (b, h)
 // Rows r >= T_b = min(seq_lens[b], cap, t_stride) are not written; nor are
 // tile_off entries j > ceil(T_b / 64).  Returns 0, or -1 on bad arguments.
+// Channel-wise magnitude pruning (R24; the channel-wise direction of the
+// pages' pruning variants, [README] "Part II"), compressed into the bitmap
+// format: each channel of a full 64-row tile keeps its kc = keep / 2 largest
+// entries over the tile's rows (the per-token rule applied to the column,
+// ties to the earlier row), so a full tile stores 64 * keep values; rows of a
+// final partial tile are pruned per token to keep.  keep must be even.
+int orc_compress_channel(const uint16_t* dense, int B, int H, int64_t t_stride, int d,
+                         const int32_t* seq_lens, int keep, int64_t cap, uint64_t* bitmaps,
+                         uint16_t* values, uint32_t* tile_off, int nthreads) {
+  if (d <= 0 || d % 64 != 0 || keep < 0 || keep > d || keep % 2 != 0 || cap <= 0 || cap % 64 != 0)
+    return -1;
+  const int words = d / 64;
+  const int kc = keep / 2;
+  const int64_t ntile_entries = cap / 64 + 1;
+  if (nthreads <= 0) nthreads = hw_threads();
+  parallel_for(static_cast<int64_t>(B) * H, nthreads, [&](int64_t u) {
+    const int64_t b = u / H;
+    const int T = clamp_len(seq_lens[b], std::min<int64_t>(cap, t_stride));
+    const uint16_t* src = dense + u * t_stride * d;
+    uint64_t* bm = bitmaps + u * cap * words;
+    uint16_t* val = values + u * cap * keep;
+    uint32_t* toff = tile_off + u * ntile_entries;
+    std::vector<uint8_t> keep_mask(static_cast<size_t>(64) * d), col_keep(64);
+    std::vector<uint16_t> col(64);
+    uint32_t count = 0;
+    for (int t0 = 0; t0 < T; t0 += 64) {
+      toff[t0 / 64] = count;
+      const int n = std::min(64, T - t0);
+      if (n == 64) {
+        for (int c = 0; c < d; ++c) {
+          for (int r = 0; r < 64; ++r) col[r] = src[static_cast<int64_t>(t0 + r) * d + c];
+          prune_row(col.data(), 64, kc, col_keep.data());
+          for (int r = 0; r < 64; ++r) keep_mask[static_cast<size_t>(r) * d + c] = col_keep[r];
+        }
+      } else {
+        for (int r = 0; r < n; ++r)
+          prune_row(src + static_cast<int64_t>(t0 + r) * d, d, keep, &keep_mask[static_cast<size_t>(r) * d]);
+      }
+      for (int r = 0; r < n; ++r) {
+        const uint16_t* x = src + static_cast<int64_t>(t0 + r) * d;
+        uint64_t* w = bm + static_cast<int64_t>(t0 + r) * words;
+        for (int i = 0; i < words; ++i) w[i] = 0;
+        for (int c = 0; c < d; ++c) {
+          if (keep_mask[static_cast<size_t>(r) * d + c]) {
+            w[c / 64] |= uint64_t{1} << (c % 64);
+            val[count++] = x[c];
+          }
+        }
+      }
+    }
+    toff[(T + 63) / 64] = count;
+  });
+  return 0;
+}
+
 // With head_keep (R22) head h keeps head_keep[h] per row and the values of
 // (b, h) start at Layout::region(b, h); values is then [B][cap * S].
 static int compress_rule(const uint16_t* dense, int B, int H, int64_t t_stride, int d,

@@ -446,3 +446,62 @@ def test_compress_24_layout_and_attention():
     ref = _sdpa_f64(q, Km[:, :, :T], Vm[:, :, :T], seq, 1.0 / math.sqrt(128))
     got = oracle.attention_compressed(q, kc, vc, seq, 1.0 / math.sqrt(128))
     assert np.abs(got - ref).max() < 1e-12
+
+
+# ---------------------------------------------------------------- channel-wise pruning (R24)
+def test_channel_wise_rule_invariants_and_layout():
+    """Full 64-row tiles: every channel keeps exactly keep/2 rows, no pruned entry
+    of a column outranks a kept one, and equal keys go to the earlier row (these
+    three properties determine the kept set); rows of the final partial tile
+    follow the per-token rule; values and tile offsets follow the format."""
+    rng = np.random.default_rng(41)
+    B, H, T, keep = 2, 2, 150, 38
+    x = rng.standard_normal((B, H, T, 128)).astype(np.float16)
+    x[0, 0, :64, 7] = np.float16(0.5)                    # a column of equal keys
+    x[1, 1, 64:128, 90] = np.where(np.arange(64) % 2, 1.0, -1.0)  # +-1: equal magnitudes
+    x = x.view(np.uint16)
+    seq = np.array([150, 128], np.int32)
+    c = oracle.compress_channel(x, seq, keep, cap=192)
+    dec = oracle.decompress(c, seq)
+    kc = keep // 2
+    for b in range(B):
+        T_b = int(seq[b])
+        for h in range(H):
+            kept = np.zeros((T_b, 128), bool)
+            for r in range(T_b):
+                w = c.bitmaps[b, h, r]
+                kept[r] = [(int(w[ch // 64]) >> (ch % 64)) & 1 for ch in range(128)]
+            for t0 in range(0, T_b - T_b % 64, 64):
+                key = (x[b, h, t0:t0 + 64] & 0x7FFF).astype(np.int64)
+                kt = kept[t0:t0 + 64]
+                assert (kt.sum(0) == kc).all()
+                for ch in range(128):
+                    kk, pk = key[kt[:, ch], ch], key[~kt[:, ch], ch]
+                    assert kk.min() >= pk.max()
+                    tau = kk.min()
+                    if (pk == tau).any():
+                        assert np.nonzero(kt[:, ch] & (key[:, ch] == tau))[0].max() < \
+                            np.nonzero(~kt[:, ch] & (key[:, ch] == tau))[0].min()
+            tail = T_b - T_b % 64
+            if tail < T_b:
+                assert np.array_equal(kept[tail:], oracle.prune_rows(x[b, h, tail:T_b], keep) == 1)
+            # format: kept values row by row in channel order, offsets = popcount prefix
+            flat = x[b, h, :T_b][kept]
+            assert np.array_equal(c.values[b, h, :flat.size], flat)
+            pc = kept.sum(1)
+            nt = (T_b + 63) // 64
+            assert c.tile_off[b, h, :nt + 1].tolist() == [int(pc[:min(64 * j, T_b)].sum())
+                                                           for j in range(nt + 1)]
+            assert np.array_equal(dec[b, h, :T_b], np.where(kept, x[b, h, :T_b], 0))
+    assert c.values.shape[-1] == 192 * keep
+
+
+def test_channel_wise_attention_equals_sdpa_on_zero_masked_cache():
+    rng = np.random.default_rng(42)
+    B, Hq, Hkv, T = 2, 4, 2, 200
+    q, K, V = _rand_inputs(rng, B, Hq, Hkv, T)
+    seq = np.array([200, 64], np.int32)
+    kc, vc = oracle.compress_channel(K, seq, 38, cap=256), oracle.compress_channel(V, seq, 64, cap=256)
+    Km, Vm = oracle.decompress(kc, seq), oracle.decompress(vc, seq)
+    ref = _sdpa_f64(q, Km[:, :, :T], Vm[:, :, :T], seq, 0.0883)
+    assert np.abs(oracle.attention_compressed(q, kc, vc, seq, 0.0883) - ref).max() < 1e-12
