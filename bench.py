@@ -403,6 +403,39 @@ def main() -> int:
         f"({hk_bytes / hk_s / 1e9:.0f} GB/s, {hk_bytes} bytes)")
     del kch, vch
 
+    # dense attention over layer 0's unpruned caches: the reference the pruned
+    # variants below are compared with
+    wsd0 = usk.make_workspace(B, Hq, Hkv, T0)
+    outd0 = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+    usk.dense_decode_attn(q_last, K0, V0, seq_h, T0, scale, outd0, wsd0)
+    torch.cuda.synchronize()
+    ref_d = outd0.float()
+    del wsd0
+
+    def dist(o):
+        return float(torch.linalg.norm(o.float() - ref_d) / torch.linalg.norm(ref_d))
+
+    # ---- channel-wise pruning at 70%: layer 0's dense caches, each channel of a
+    # 64-row tile keeps 19 rows (38 values per row on average, the same bytes)
+    kcw = usk.CompressedKV(B, Hkv, keep, cap, dev)
+    vcw = usk.CompressedKV(B, Hkv, keep, cap, dev)
+    cw_pre = median(timed(lambda: (usk.prune_compress_channel(kcw, K0, seq_h),
+                                   usk.prune_compress_channel(vcw, V0, seq_h)), 3))
+    cw_s = median(timed(lambda: usk.decode_attn(q_last, kcw, vcw, seq_h, cap, scale, out, ws), 10,
+                        before=lambda: usk.probe_stream_read(flush, sink)))
+    cw_bytes = kcw.used_bytes(sh0) + vcw.used_bytes(sh0)
+    cw_dist = dist(out)
+    ktk = usk.CompressedKV(B, Hkv, keep, cap, dev)
+    vtk = usk.CompressedKV(B, Hkv, keep, cap, dev)
+    usk.prune_compress(ktk, K0, seq_h)
+    usk.prune_compress(vtk, V0, seq_h)
+    usk.decode_attn(q_last, ktk, vtk, seq_h, cap, scale, out, ws)
+    tok_dist = dist(out)
+    log(f"channel-wise pruning, keep {keep}: prefill K and V {cw_pre * 1e6:.0f} us; decode after a "
+        f"1 GiB read {cw_s * 1e6:.1f} us ({cw_bytes / cw_s / 1e9:.0f} GB/s); relative L2 distance "
+        f"to dense attention {cw_dist:.4f} (per-token pruning at the same keep: {tok_dist:.4f})")
+    del kcw, vcw, ktk, vtk
+
     # ---- 2:4 comparator at 50%: layer 0's dense caches pruned 2:4 and pruned
     # per token to keep 64 (the same bytes); the 2:4 kernel and the unstructured
     # kernel on the 2:4 caches, the unstructured kernel on its own caches; each
@@ -427,15 +460,10 @@ def main() -> int:
         outs50[name] = out.float().clone()
         cmp50[name] = t_
         log(f"50% sparsity, {name}: {t_ * 1e6:.1f} us ({b50 / t_ / 1e9:.0f} GB/s)")
-    wsd0 = usk.make_workspace(B, Hq, Hkv, T0)
-    outd0 = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
-    usk.dense_decode_attn(q_last, K0, V0, seq_h, T0, scale, outd0, wsd0)
-    torch.cuda.synchronize()
-    ref_d = outd0.float()
-    err50 = {n: float(torch.linalg.norm(o - ref_d) / torch.linalg.norm(ref_d)) for n, o in outs50.items()}
+    err50 = {n: dist(o) for n, o in outs50.items()}
     for n, e in err50.items():
         log(f"50% sparsity, {n}: relative L2 distance to dense attention {e:.4f}")
-    del k24, v24, k64, v64, wsd0
+    del k24, v24, k64, v64
 
     # ---- dense fp16 comparison kernel (layer 0's caches, unpruned), batch 8 and batch 6
     dense = {}
@@ -541,6 +569,11 @@ def main() -> int:
             "head_keep_v": vheads,
             "head_keep_decode_us_after_1gib_read": round(hk_s * 1e6, 2),
             "head_keep_decode_gbs_after_1gib_read": round(hk_bytes / hk_s / 1e9, 1),
+            "channel_wise_prefill_us": round(cw_pre * 1e6, 1),
+            "channel_wise_decode_us_after_1gib_read": round(cw_s * 1e6, 2),
+            "channel_wise_decode_gbs_after_1gib_read": round(cw_bytes / cw_s / 1e9, 1),
+            "sparsity70_rel_l2_to_dense": {"per-token": round(tok_dist, 5),
+                                           "channel-wise": round(cw_dist, 5)},
             "sparsity50_bytes": int(b50),
             "sparsity50_us_after_1gib_read": {n: round(t_ * 1e6, 2) for n, t_ in cmp50.items()},
             "sparsity50_rel_l2_to_dense": {n: round(e, 5) for n, e in err50.items()},

@@ -87,9 +87,11 @@ typedef enum {
  * keep different from their maximum, return MUSTAFAR_EINVAL.
  * batch * num_kv_heads must stay below 2^31.  Calls that break these limits
  * return MUSTAFAR_EINVAL (MUSTAFAR_EUNSUPPORTED for another head_dim).
- * The decode calls also accept rows holding fewer than keep values (values
- * still packed back to back, tile_offsets consistent with the popcounts);
- * rows must not hold more than keep.
+ * The decode calls read any cache in this format: rows may hold any number of
+ * values from 0 to head_dim (channel-wise pruning stores rows of varying
+ * length) as long as the values are packed back to back, tile_offsets are
+ * consistent with the popcounts and a (batch, head) stores at most
+ * capacity * keep values.
  */
 typedef struct {
   int32_t batch;
@@ -275,6 +277,22 @@ int mustafar_decode_step(const uint16_t *q, int32_t num_q_heads, const mustafar_
                          int32_t *seq_lens, uint32_t *status, int32_t max_seq_len, float scale,
                          int32_t splits, uint16_t *out, void *workspace, uint64_t workspace_bytes,
                          void *stream);
+
+/*
+ * Channel-wise magnitude pruning, prefill (the channel-wise direction of the
+ * pruning variants in [README] "Part II"; the pages give no grouping, so this
+ * library groups by its 64-row tiles): in every full 64-row tile of a
+ * (batch, head), each channel keeps its keep/2 entries of largest magnitude
+ * over the tile's rows (ties to the earlier row), so the tile stores 64 * keep
+ * values with rows of varying length; the rows of a final partial tile are
+ * pruned per token to keep (like mustafar_prune_compress), and so are the rows
+ * mustafar_append_token adds later.  The output is the bitmap format above;
+ * the decode calls read it.  keep must be even and head_keep NULL
+ * (MUSTAFAR_EINVAL otherwise); other arguments and errors as
+ * mustafar_prune_compress.
+ */
+int mustafar_prune_compress_channel(const mustafar_kv_t *dst, const uint16_t *dense,
+                                    int64_t t_stride, const int32_t *seq_lens, void *stream);
 
 /*
  * 2:4 semi-structured comparator, prefill: prunes every row of `dense` so that

@@ -30,7 +30,7 @@ EXPORTS = (
     "mustafar_decode_auto_splits", "mustafar_decode_workspace_bytes",
     "mustafar_decode_workspace_init", "mustafar_decode_attn", "mustafar_decode_attn_valu",
     "mustafar_decode_step", "mustafar_dense_decode_attn", "mustafar_probe_stream_read",
-    "mustafar_prune_compress_24", "mustafar_decode_attn_24",
+    "mustafar_prune_compress_24", "mustafar_decode_attn_24", "mustafar_prune_compress_channel",
 )
 
 
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
                                                           ctypes.c_float, I32, P, P, U64, P]),
             "mustafar_probe_stream_read": (ctypes.c_int, [P, U64, P, P]),
             "mustafar_prune_compress_24": (ctypes.c_int, [KVP, P, I64, P, P]),
+            "mustafar_prune_compress_channel": (ctypes.c_int, [KVP, P, I64, P, P]),
             "mustafar_decode_attn_24": (ctypes.c_int, [P, I32, KVP, KVP, P, I32, ctypes.c_float, I32,
                                                        P, P, U64, P]),
         }
@@ -182,6 +183,13 @@ def prune_compress(dst: CompressedKV, dense, seq_lens, stream=None) -> None:
     """dense: [B][H][t_stride][128] fp16 contiguous (device); seq_lens int32 [B] (device)."""
     assert dense.is_contiguous() and dense.shape[-1] == HEAD_DIM
     _check("mustafar_prune_compress", lib().mustafar_prune_compress(
+        dst.ref, dense.data_ptr(), dense.shape[2], seq_lens.data_ptr(), _stream(stream)))
+
+
+def prune_compress_channel(dst: CompressedKV, dense, seq_lens, stream=None) -> None:
+    """Channel-wise pruning: per full 64-row tile each channel keeps dst.keep/2 rows."""
+    assert dense.is_contiguous() and dense.shape[-1] == HEAD_DIM
+    _check("mustafar_prune_compress_channel", lib().mustafar_prune_compress_channel(
         dst.ref, dense.data_ptr(), dense.shape[2], seq_lens.data_ptr(), _stream(stream)))
 
 

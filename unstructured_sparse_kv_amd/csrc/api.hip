@@ -229,6 +229,19 @@ int mustafar_prune_compress(const mustafar_kv_t* dst, const uint16_t* dense, int
   return launched(launch_prune_compress(*dst, m, dense, t_stride, seq_lens, (hipStream_t)stream));
 }
 
+int mustafar_prune_compress_channel(const mustafar_kv_t* dst, const uint16_t* dense,
+                                    int64_t t_stride, const int32_t* seq_lens, void* stream) {
+  KeepMap m;
+  int rc = check_kv(dst, &m);
+  if (rc) return rc;
+  if (dst->keep % 2 != 0 || dst->head_keep) return MUSTAFAR_EINVAL;
+  if (!dense || !seq_lens || !aligned16(dense) || !aligned4(seq_lens)) return MUSTAFAR_EINVAL;
+  if (t_stride <= 0 || t_stride > kMaxCapacity * 64) return MUSTAFAR_EINVAL;
+  if ((rc = check_device())) return rc;
+  return launched(
+      launch_prune_compress_channel(*dst, m, dense, t_stride, seq_lens, (hipStream_t)stream));
+}
+
 int mustafar_prune_compress_24(const mustafar_kv_t* dst, const uint16_t* dense, int64_t t_stride,
                                const int32_t* seq_lens, void* stream) {
   KeepMap m;

@@ -94,42 +94,51 @@ __device__ __forceinline__ void walk_fast(const uint32_t (&row)[KW], uint4 w, in
 
 // General walk: empty dwords are compacted away (each kept dword carries its
 // channel base) and a lane that has used all its set bits reports channel 128
-// (the zero q entry / the dump row); its remaining values are zero.
-template <int NMAX, uint32_t MUL, int KW, class F>
-__device__ __forceinline__ void walk_general(const uint32_t (&row)[KW], uint4 w, int iters,
-                                             uint32_t base, F&& f) {
-  const uint32_t dump = base + 128u * MUL;
-  uint32_t cw[4] = {w.x, w.y, w.z, w.w};
-  uint32_t cb[4] = {base, base + 32u * MUL, base + 64u * MUL, base + 96u * MUL};
+// (the zero q entry / the dump row); its remaining values are zero.  The walk
+// state survives between calls of run(), so a row with more set bits than the
+// value registers hold is walked in rounds, the registers reloaded between
+// them.
+template <uint32_t MUL>
+struct GeneralWalk {
+  uint32_t cur, b0, n1, b1, n2, b2, n3, b3, dump;
+  __device__ __forceinline__ GeneralWalk(uint4 w, uint32_t base) {
+    dump = base + 128u * MUL;
+    uint32_t cw[4] = {w.x, w.y, w.z, w.w};
+    uint32_t cb[4] = {base, base + 32u * MUL, base + 64u * MUL, base + 96u * MUL};
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
+    for (int pass = 0; pass < 3; ++pass) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const bool sw = (cw[j] == 0u) && (cw[j + 1] != 0u);
-      const uint32_t a = cw[j], ab = cb[j];
-      cw[j] = sw ? cw[j + 1] : cw[j];
-      cb[j] = sw ? cb[j + 1] : cb[j];
-      cw[j + 1] = sw ? a : cw[j + 1];
-      cb[j + 1] = sw ? ab : cb[j + 1];
+      for (int j = 0; j < 3; ++j) {
+        const bool sw = (cw[j] == 0u) && (cw[j + 1] != 0u);
+        const uint32_t a = cw[j], ab = cb[j];
+        cw[j] = sw ? cw[j + 1] : cw[j];
+        cb[j] = sw ? cb[j + 1] : cb[j];
+        cw[j + 1] = sw ? a : cw[j + 1];
+        cb[j + 1] = sw ? ab : cb[j + 1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cb[j] = cw[j] ? cb[j] : dump;
+    cur = cw[0]; b0 = cb[0]; n1 = cw[1]; b1 = cb[1]; n2 = cw[2]; b2 = cb[2]; n3 = cw[3]; b3 = cb[3];
+  }
+  // The next `iters` set bits (uniform across the wave), paired with values
+  // 0 .. iters-1 of `row`.
+  template <int NMAX, int KW, class F>
+  __device__ __forceinline__ void run(const uint32_t (&row)[KW], int iters, F&& f) {
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+      if (i < iters) {
+        f(cur ? b0 + (uint32_t)__builtin_ctz(cur) * MUL : dump, value_at(row, i));
+        cur &= cur - 1u;
+        const bool z = (cur == 0u);
+        cur = z ? n1 : cur; b0 = z ? b1 : b0;
+        n1 = z ? n2 : n1; b1 = z ? b2 : b1;
+        n2 = z ? n3 : n2; b2 = z ? b3 : b2;
+        n3 = z ? 0u : n3; b3 = z ? dump : b3;
+      }
     }
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) cb[j] = cw[j] ? cb[j] : dump;
-  uint32_t cur = cw[0], b0 = cb[0], n1 = cw[1], b1 = cb[1], n2 = cw[2], b2 = cb[2], n3 = cw[3],
-           b3 = cb[3];
-#pragma unroll
-  for (int i = 0; i < NMAX; ++i) {
-    if (i < iters) {
-      f(cur ? b0 + (uint32_t)__builtin_ctz(cur) * MUL : dump, value_at(row, i));
-      cur &= cur - 1u;
-      const bool z = (cur == 0u);
-      cur = z ? n1 : cur; b0 = z ? b1 : b0;
-      n1 = z ? n2 : n1; b1 = z ? b2 : b1;
-      n2 = z ? n3 : n2; b2 = z ? b3 : b2;
-      n3 = z ? 0u : n3; b3 = z ? dump : b3;
-    }
-  }
-}
+};
 
 // Loads dwords of the stored values from half index `start` of the region
 // and shifts them so that row[i] holds values 2i and 2i+1 of the row.
@@ -222,12 +231,26 @@ __device__ __forceinline__ void decode_side(__amdgpu_buffer_rsrc_t rs, uint32_t 
   const uint32_t pc = valid ? pop : 0u;
   const uint32_t st = toff + wave_excl_scan(pc);
   const int iters = (int)wave_uniform(wave_max_u32(pc));
-  uint32_t r[KW];
-  load_row<KW>(rs, st, row_chunks(iters), true, r);
-  mask_row<KW>(r, pc);
-  patch(r);
-  const uint4 b = valid ? bm : make_uint4(0u, 0u, 0u, 0u);
-  walk_general<NMAX, MUL>(r, b, iters, base, f);
+  GeneralWalk<MUL> walk(valid ? bm : make_uint4(0u, 0u, 0u, 0u), base);
+  {
+    const int n = iters < NMAX ? iters : NMAX;
+    uint32_t r[KW];
+    load_row<KW>(rs, st, row_chunks(n), true, r);
+    mask_row<KW>(r, pc);
+    patch(r);
+    walk.template run<NMAX>(r, n, f);
+  }
+  // further rounds of at most NMAX values for rows holding more (rows may hold
+  // more values than keep, e.g. after channel-wise pruning)
+  if (__builtin_expect(iters > NMAX, 0)) {
+    for (int done = NMAX; done < iters; done += NMAX) {
+      const int n = iters - done < NMAX ? iters - done : NMAX;
+      uint32_t r[KW];
+      load_row<KW>(rs, st + (uint32_t)done, row_chunks(n), true, r);
+      mask_row<KW>(r, pc > (uint32_t)done ? pc - (uint32_t)done : 0u);
+      walk.template run<NMAX>(r, n, f);
+    }
+  }
 }
 
 }  // namespace mustafar

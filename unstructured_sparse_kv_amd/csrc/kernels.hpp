@@ -138,6 +138,9 @@ inline uint64_t workspace_partial_bytes(int64_t batch, int64_t hq, int64_t split
 hipError_t launch_prune_compress(const mustafar_kv_t& dst, const KeepMap& map, const uint16_t* dense,
                                  int64_t t_stride, const int32_t* seq_lens, hipStream_t stream,
                                  bool two_four = false);
+hipError_t launch_prune_compress_channel(const mustafar_kv_t& dst, const KeepMap& map,
+                                         const uint16_t* dense, int64_t t_stride,
+                                         const int32_t* seq_lens, hipStream_t stream);
 hipError_t launch_append(const mustafar_kv_t& k, const KeepMap& kmap, const mustafar_kv_t& v,
                          const KeepMap& vmap, const uint16_t* k_new, const uint16_t* v_new,
                          int32_t* seq_lens, uint32_t* status, hipStream_t stream);
