@@ -78,8 +78,11 @@ __host__ __device__ constexpr uint64_t lut_entry(uint32_t n) {
   return (uint64_t)lo | ((uint64_t)hi << 32);
 }
 
+// Two waves per SIMD (the LDS footprint allows no more): at most 256 registers
+// per lane, accumulation registers included.
 template <int G>
-__global__ __launch_bounds__(kDecodeBlock) void decode_24_kernel(SparseDecodeArgs a) {
+__global__ __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_24_kernel(SparseDecodeArgs a) {
   using C = Cfg24<G>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 

@@ -86,8 +86,14 @@ __device__ __forceinline__ void append_row(const uint16_t* src, int keep, uint64
   wave_lds_sync();
 }
 
+// Two waves per SIMD is what the LDS footprint allows.  The 64-value variants
+// are held to the matching register budget (256 per lane, accumulation
+// registers included), which they would otherwise exceed; the others fit it
+// unasked (the hint measurably slows the 38-value variant's schedule), and
+// rows of up to 128 values run at one wave per SIMD.
 template <int G, int KMAX, int NK>
-__global__ __launch_bounds__(kDecodeBlock) void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
+__global__ __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_waves_per_eu(KMAX == 64 ? 2 : 1)))
+void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
   constexpr int NMAX = NK > 0 ? NK : KMAX;
   constexpr int KW = RowCfg<NMAX>::kW;
   using C = MfmaCfg<G, KW>;
