@@ -196,6 +196,8 @@ def main() -> int:
                     help="seconds of read-only decode calls before the warmup steps (clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the per-head keep, channel-wise and 2:4 measurements")
     ap.add_argument("--stack-sweep", action="store_true",
                     help="instead of the benchmark: the 32-layer stack batch x length sweep")
     ap.add_argument("--layers", type=int, default=3,
@@ -385,85 +387,104 @@ def main() -> int:
     log(f"vector-unit sparse decode (mustafar_decode_attn_valu), after a 1 GiB read: "
         f"{valu_s * 1e6:.1f} us")
 
-    # ---- per-head keep: layer 0's dense caches pruned with a keep per kv head
-    # (mean 38, so the same bytes as the uniform layer); the bucketed walk runs
-    kheads = [28, 32, 34, 38, 38, 42, 44, 48]
-    vheads = kheads[::-1]
-    seq_h = torch.full((B,), T0, dtype=torch.int32, device=dev)
-    kch = usk.CompressedKV(B, Hkv, None, cap, dev, head_keep=kheads)
-    vch = usk.CompressedKV(B, Hkv, None, cap, dev, head_keep=vheads)
-    usk.prune_compress(kch, K0, seq_h)
-    usk.prune_compress(vch, V0, seq_h)
-    torch.cuda.synchronize()
-    hk_s = median(timed(lambda: usk.decode_attn(q_last, kch, vch, seq_h, cap, scale, out, ws), 10,
-                        before=lambda: usk.probe_stream_read(flush, sink)))
-    sh0 = np.full(B, T0, np.int32)
-    hk_bytes = kch.used_bytes(sh0) + vch.used_bytes(sh0)
-    log(f"per-head keep K {kheads} / V {vheads}: decode after a 1 GiB read {hk_s * 1e6:.1f} us "
-        f"({hk_bytes / hk_s / 1e9:.0f} GB/s, {hk_bytes} bytes)")
-    del kch, vch
+    def variants():
+        """Per-head keep, channel-wise pruning and the 2:4 comparator on layer 0's dense caches."""
+        # ---- per-head keep: layer 0's dense caches pruned with a keep per kv head
+        # (mean 38, so the same bytes as the uniform layer); the bucketed walk runs
+        kheads = [28, 32, 34, 38, 38, 42, 44, 48]
+        vheads = kheads[::-1]
+        seq_h = torch.full((B,), T0, dtype=torch.int32, device=dev)
+        kch = usk.CompressedKV(B, Hkv, None, cap, dev, head_keep=kheads)
+        vch = usk.CompressedKV(B, Hkv, None, cap, dev, head_keep=vheads)
+        usk.prune_compress(kch, K0, seq_h)
+        usk.prune_compress(vch, V0, seq_h)
+        torch.cuda.synchronize()
+        hk_s = median(timed(lambda: usk.decode_attn(q_last, kch, vch, seq_h, cap, scale, out, ws), 10,
+                            before=lambda: usk.probe_stream_read(flush, sink)))
+        sh0 = np.full(B, T0, np.int32)
+        hk_bytes = kch.used_bytes(sh0) + vch.used_bytes(sh0)
+        log(f"per-head keep K {kheads} / V {vheads}: decode after a 1 GiB read {hk_s * 1e6:.1f} us "
+            f"({hk_bytes / hk_s / 1e9:.0f} GB/s, {hk_bytes} bytes)")
+        del kch, vch
 
-    # dense attention over layer 0's unpruned caches: the reference the pruned
-    # variants below are compared with
-    wsd0 = usk.make_workspace(B, Hq, Hkv, T0)
-    outd0 = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
-    usk.dense_decode_attn(q_last, K0, V0, seq_h, T0, scale, outd0, wsd0)
-    torch.cuda.synchronize()
-    ref_d = outd0.float()
-    del wsd0
+        # dense attention over layer 0's unpruned caches: the reference the pruned
+        # variants below are compared with
+        wsd0 = usk.make_workspace(B, Hq, Hkv, T0)
+        outd0 = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+        usk.dense_decode_attn(q_last, K0, V0, seq_h, T0, scale, outd0, wsd0)
+        torch.cuda.synchronize()
+        ref_d = outd0.float()
+        del wsd0
 
-    def dist(o):
-        return float(torch.linalg.norm(o.float() - ref_d) / torch.linalg.norm(ref_d))
+        def dist(o):
+            return float(torch.linalg.norm(o.float() - ref_d) / torch.linalg.norm(ref_d))
 
-    # ---- channel-wise pruning at 70%: layer 0's dense caches, each channel of a
-    # 64-row tile keeps 19 rows (38 values per row on average, the same bytes)
-    kcw = usk.CompressedKV(B, Hkv, keep, cap, dev)
-    vcw = usk.CompressedKV(B, Hkv, keep, cap, dev)
-    cw_pre = median(timed(lambda: (usk.prune_compress_channel(kcw, K0, seq_h),
-                                   usk.prune_compress_channel(vcw, V0, seq_h)), 3))
-    cw_s = median(timed(lambda: usk.decode_attn(q_last, kcw, vcw, seq_h, cap, scale, out, ws), 10,
-                        before=lambda: usk.probe_stream_read(flush, sink)))
-    cw_bytes = kcw.used_bytes(sh0) + vcw.used_bytes(sh0)
-    cw_dist = dist(out)
-    ktk = usk.CompressedKV(B, Hkv, keep, cap, dev)
-    vtk = usk.CompressedKV(B, Hkv, keep, cap, dev)
-    usk.prune_compress(ktk, K0, seq_h)
-    usk.prune_compress(vtk, V0, seq_h)
-    usk.decode_attn(q_last, ktk, vtk, seq_h, cap, scale, out, ws)
-    tok_dist = dist(out)
-    log(f"channel-wise pruning, keep {keep}: prefill K and V {cw_pre * 1e6:.0f} us; decode after a "
-        f"1 GiB read {cw_s * 1e6:.1f} us ({cw_bytes / cw_s / 1e9:.0f} GB/s); relative L2 distance "
-        f"to dense attention {cw_dist:.4f} (per-token pruning at the same keep: {tok_dist:.4f})")
-    del kcw, vcw, ktk, vtk
+        # ---- channel-wise pruning at 70%: layer 0's dense caches, each channel of a
+        # 64-row tile keeps 19 rows (38 values per row on average, the same bytes)
+        kcw = usk.CompressedKV(B, Hkv, keep, cap, dev)
+        vcw = usk.CompressedKV(B, Hkv, keep, cap, dev)
+        cw_pre = median(timed(lambda: (usk.prune_compress_channel(kcw, K0, seq_h),
+                                       usk.prune_compress_channel(vcw, V0, seq_h)), 3))
+        cw_s = median(timed(lambda: usk.decode_attn(q_last, kcw, vcw, seq_h, cap, scale, out, ws), 10,
+                            before=lambda: usk.probe_stream_read(flush, sink)))
+        cw_bytes = kcw.used_bytes(sh0) + vcw.used_bytes(sh0)
+        cw_dist = dist(out)
+        ktk = usk.CompressedKV(B, Hkv, keep, cap, dev)
+        vtk = usk.CompressedKV(B, Hkv, keep, cap, dev)
+        usk.prune_compress(ktk, K0, seq_h)
+        usk.prune_compress(vtk, V0, seq_h)
+        usk.decode_attn(q_last, ktk, vtk, seq_h, cap, scale, out, ws)
+        tok_dist = dist(out)
+        log(f"channel-wise pruning, keep {keep}: prefill K and V {cw_pre * 1e6:.0f} us; decode after a "
+            f"1 GiB read {cw_s * 1e6:.1f} us ({cw_bytes / cw_s / 1e9:.0f} GB/s); relative L2 distance "
+            f"to dense attention {cw_dist:.4f} (per-token pruning at the same keep: {tok_dist:.4f})")
+        del kcw, vcw, ktk, vtk
 
-    # ---- 2:4 comparator at 50%: layer 0's dense caches pruned 2:4 and pruned
-    # per token to keep 64 (the same bytes); the 2:4 kernel and the unstructured
-    # kernel on the 2:4 caches, the unstructured kernel on its own caches; each
-    # output's distance to the dense attention over the unpruned caches
-    k24 = usk.CompressedKV(B, Hkv, 64, cap, dev)
-    v24 = usk.CompressedKV(B, Hkv, 64, cap, dev)
-    usk.prune_compress_24(k24, K0, seq_h)
-    usk.prune_compress_24(v24, V0, seq_h)
-    k64 = usk.CompressedKV(B, Hkv, 64, cap, dev)
-    v64 = usk.CompressedKV(B, Hkv, 64, cap, dev)
-    usk.prune_compress(k64, K0, seq_h)
-    usk.prune_compress(v64, V0, seq_h)
-    torch.cuda.synchronize()
-    b50 = k24.used_bytes(sh0) + v24.used_bytes(sh0)
-    cmp50 = {}
-    outs50 = {}
-    for name, fn, kc_, vc_ in (("2:4 kernel, 2:4 caches", usk.decode_attn_24, k24, v24),
-                               ("unstructured kernel, 2:4 caches", usk.decode_attn, k24, v24),
-                               ("unstructured kernel, keep-64 caches", usk.decode_attn, k64, v64)):
-        t_ = median(timed(lambda: fn(q_last, kc_, vc_, seq_h, cap, scale, out, ws), 10,
-                          before=lambda: usk.probe_stream_read(flush, sink)))
-        outs50[name] = out.float().clone()
-        cmp50[name] = t_
-        log(f"50% sparsity, {name}: {t_ * 1e6:.1f} us ({b50 / t_ / 1e9:.0f} GB/s)")
-    err50 = {n: dist(o) for n, o in outs50.items()}
-    for n, e in err50.items():
-        log(f"50% sparsity, {n}: relative L2 distance to dense attention {e:.4f}")
-    del k24, v24, k64, v64
+        # ---- 2:4 comparator at 50%: layer 0's dense caches pruned 2:4 and pruned
+        # per token to keep 64 (the same bytes); the 2:4 kernel and the unstructured
+        # kernel on the 2:4 caches, the unstructured kernel on its own caches; each
+        # output's distance to the dense attention over the unpruned caches
+        k24 = usk.CompressedKV(B, Hkv, 64, cap, dev)
+        v24 = usk.CompressedKV(B, Hkv, 64, cap, dev)
+        usk.prune_compress_24(k24, K0, seq_h)
+        usk.prune_compress_24(v24, V0, seq_h)
+        k64 = usk.CompressedKV(B, Hkv, 64, cap, dev)
+        v64 = usk.CompressedKV(B, Hkv, 64, cap, dev)
+        usk.prune_compress(k64, K0, seq_h)
+        usk.prune_compress(v64, V0, seq_h)
+        torch.cuda.synchronize()
+        b50 = k24.used_bytes(sh0) + v24.used_bytes(sh0)
+        cmp50 = {}
+        outs50 = {}
+        for name, fn, kc_, vc_ in (("2:4 kernel, 2:4 caches", usk.decode_attn_24, k24, v24),
+                                   ("unstructured kernel, 2:4 caches", usk.decode_attn, k24, v24),
+                                   ("unstructured kernel, keep-64 caches", usk.decode_attn, k64, v64)):
+            t_ = median(timed(lambda: fn(q_last, kc_, vc_, seq_h, cap, scale, out, ws), 10,
+                              before=lambda: usk.probe_stream_read(flush, sink)))
+            outs50[name] = out.float().clone()
+            cmp50[name] = t_
+            log(f"50% sparsity, {name}: {t_ * 1e6:.1f} us ({b50 / t_ / 1e9:.0f} GB/s)")
+        err50 = {n: dist(o) for n, o in outs50.items()}
+        for n, e in err50.items():
+            log(f"50% sparsity, {n}: relative L2 distance to dense attention {e:.4f}")
+        del k24, v24, k64, v64
+
+        return {
+            "head_keep_k": kheads,
+            "head_keep_v": vheads,
+            "head_keep_decode_us_after_1gib_read": round(hk_s * 1e6, 2),
+            "head_keep_decode_gbs_after_1gib_read": round(hk_bytes / hk_s / 1e9, 1),
+            "channel_wise_prefill_us": round(cw_pre * 1e6, 1),
+            "channel_wise_decode_us_after_1gib_read": round(cw_s * 1e6, 2),
+            "channel_wise_decode_gbs_after_1gib_read": round(cw_bytes / cw_s / 1e9, 1),
+            "sparsity70_rel_l2_to_dense": {"per-token": round(tok_dist, 5),
+                                           "channel-wise": round(cw_dist, 5)},
+            "sparsity50_bytes": int(b50),
+            "sparsity50_us_after_1gib_read": {n: round(t_ * 1e6, 2) for n, t_ in cmp50.items()},
+            "sparsity50_rel_l2_to_dense": {n: round(e, 5) for n, e in err50.items()},
+        }
+
+    var_extra = {} if args.no_variants else variants()
 
     # ---- dense fp16 comparison kernel (layer 0's caches, unpruned), batch 8 and batch 6
     dense = {}
@@ -565,20 +586,9 @@ def main() -> int:
             "prefill_gbs_moved": round((dense_bytes0 + comp_bytes0) / prefill_s / 1e9, 1),
             "parity_last_step": parity,
             "clock_ramp_decode_calls": ramp_calls,
-            "head_keep_k": kheads,
-            "head_keep_v": vheads,
-            "head_keep_decode_us_after_1gib_read": round(hk_s * 1e6, 2),
-            "head_keep_decode_gbs_after_1gib_read": round(hk_bytes / hk_s / 1e9, 1),
-            "channel_wise_prefill_us": round(cw_pre * 1e6, 1),
-            "channel_wise_decode_us_after_1gib_read": round(cw_s * 1e6, 2),
-            "channel_wise_decode_gbs_after_1gib_read": round(cw_bytes / cw_s / 1e9, 1),
-            "sparsity70_rel_l2_to_dense": {"per-token": round(tok_dist, 5),
-                                           "channel-wise": round(cw_dist, 5)},
-            "sparsity50_bytes": int(b50),
-            "sparsity50_us_after_1gib_read": {n: round(t_ * 1e6, 2) for n, t_ in cmp50.items()},
-            "sparsity50_rel_l2_to_dense": {n: round(e, 5) for n, e in err50.items()},
         },
     }
+    res["extra"].update(var_extra)
     if dense:
         res["extra"].update({
             "dense_us_b8_after_1gib_read": round(dense[8] * 1e6, 2),
