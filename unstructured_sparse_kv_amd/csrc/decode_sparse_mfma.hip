@@ -27,7 +27,12 @@
 //   P.V         v_mfma_f32_16x16x32_f16: A = 16 channels x 32 rows of V,
 //               B = p[rows][heads]; accumulators out[channel][head] stay in
 //               registers for the whole split (8 channel blocks x 2 row blocks).
-// The strides make every MFMA operand read an optimal 8-cycle ds_read_b128.
+// The MFMA operands are read with ds_wrxchg_rtn_b64, which returns the 8 bytes
+// and leaves zeros: the operand reads of a tile cover every byte its walk can
+// write, so the buffer is clean for the next tile without a clearing pass.
+// Lanes past the end of the sequence therefore write zeros (into their own row
+// or column), never data outside the operand area.  The strides keep the
+// operand reads free of bank conflicts.
 #include "decode_walk.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -40,15 +45,10 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kKRow = 272;  // key tile row: 128 fp16 + 16 B (dump slot, bank spread)
+constexpr uint32_t kKRow = 272;  // key tile row: 128 fp16 + 16 B (general-walk dump slot, bank spread)
 constexpr uint32_t kVRow = 144;  // value tile channel row: 64 fp16 + 16 B
-constexpr int kTileBytes = 129 * 144;  // value tile + dump row; the key tile (64 x 272) fits too
-// Writes of lanes past the end of the sequence: a key row after the 64 tile
-// rows (free while the key tile is in use) and, for values, the padding
-// column 64 of every channel row.
-constexpr uint32_t kKDump = 64 * kKRow;
-constexpr uint32_t kVDump = 128;
-static_assert(kKDump + kKRow <= (uint32_t)kTileBytes, "key dump row inside the tile buffer");
+// value tile + the general walk's dump row (channel 128); the key tile (64 x 272) fits too
+constexpr int kTileBytes = 129 * 144;
 constexpr float kRescaleSlack = 8.f;   // log2 units
 
 template <int G, int KW>
@@ -213,6 +213,17 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
     issue_v(tb, vt0);
   }
   const uint32_t tile_base = (uint32_t)(tile_lds - smem);
+  // the buffer starts clean; afterwards the operand reads clear it
+  for (uint32_t o = 8u * lane; o < (uint32_t)kTileBytes; o += 8u * kWave)
+    *reinterpret_cast<uint2*>(tile_lds + o) = make_uint2(0u, 0u);
+  wave_lds_sync();
+  // An MFMA operand (16 bytes) read and cleared.
+  auto take16 = [&](const char* p) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<char*>(p));
+    const uint64_t lo = __hip_atomic_exchange(q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    const uint64_t hi = __hip_atomic_exchange(q + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+  };
   auto scatter = [&](uint32_t addr, uint32_t vbits) {
     *reinterpret_cast<uint16_t*>(smem + addr) = (uint16_t)vbits;
   };
@@ -225,16 +236,11 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
     offsets(nxt, kt0n, vt0n);
 
     // ---- key tile K[t][c]
-    wave_lds_sync();  // the previous tile's reads of the buffer are done
-#pragma unroll
-    for (int j = 0; j < 32; ++j)  // 2 rows of 256 B per instruction; the row padding stays as is
-      *reinterpret_cast<uint2*>(tile_lds + (2 * j + (lane >> 5)) * kKRow + 8 * (lane & 31u)) =
-          make_uint2(0u, 0u);
-    wave_lds_sync();
+    wave_lds_sync();  // the previous tile's reads (and clears) of the buffer are done
     take_new(tile, new_lds, kb, krow);
-    decode_side<NMAX, NK, true, 2u>(krs, kt0, kk, valid, partial, !kEvenExact || !(kt0 & 1u), kb,
-                                    krow, tile_base + lane * kKRow, tile_base + kKDump, scatter,
-                                    [&](uint32_t (&r)[KW]) { uint4 t; take_new(tile, new_lds, t, r); });
+    decode_side<NMAX, NK, false, 2u>(krs, kt0, kk, valid, partial, !kEvenExact || !(kt0 & 1u), kb,
+                                     krow, tile_base + lane * kKRow, 0u, scatter,
+                                     [&](uint32_t (&r)[KW]) { uint4 t; take_new(tile, new_lds, t, r); });
     issue_k(nxt, kt0n);
     wave_lds_sync();
 
@@ -246,7 +252,7 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
       const char* rowp = tile_lds + (16 * mb + l16) * kKRow + 16 * grp;
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(rowp + 64 * kb4);
+        const uint4 x = take16(rowp + 64 * kb4);
         cs[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, x), bq[kb4],
                                                         cs[mb], 0, 0, 0);
       }
@@ -302,15 +308,10 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
 
     // ---- value tile V[c][t] in the same buffer
     wave_lds_sync();  // score reads of the key tile done; p written
-#pragma unroll
-    for (int j = 0; j < 32; ++j)  // 4 channel rows of 128 B per instruction
-      *reinterpret_cast<uint2*>(tile_lds + (4 * j + (lane >> 4)) * kVRow + 8 * (lane & 15u)) =
-          make_uint2(0u, 0u);
-    wave_lds_sync();
     take_new(tile, new_lds + C::kNewSide, vb, vrow);
-    decode_side<NMAX, NK, true, kVRow>(
+    decode_side<NMAX, NK, false, kVRow>(
         vrs, vt0, vk, valid, partial, !kEvenExact || !(vt0 & 1u), vb, vrow, tile_base + 2u * lane,
-        tile_base + kVDump, scatter,
+        0u, scatter,
         [&](uint32_t (&r)[KW]) { uint4 t; take_new(tile, new_lds + C::kNewSide, t, r); });
     issue_v(nxt, vt0n);
     wave_lds_sync();
@@ -322,8 +323,8 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       const char* vrowp = tile_lds + (16 * mb + l16) * kVRow + 16 * grp;
-      const uint4 x0 = *reinterpret_cast<const uint4*>(vrowp);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(vrowp + 64);
+      const uint4 x0 = take16(vrowp);
+      const uint4 x1 = take16(vrowp + 64);
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, x0), pb0, acc[mb],
                                                        0, 0, 0);
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, x1), pb1, acc[mb],
