@@ -181,8 +181,9 @@ int mustafar_append_token(const mustafar_kv_t *k, const mustafar_kv_t *v, const 
  * Splits over the sequence that mustafar_decode_attn and mustafar_decode_attn_valu
  * use when called with splits = 0, for this shape: floor(512 / (batch *
  * num_kv_heads)) splits, so at most 512 blocks of 4 waves (two per compute
- * unit of an MI355X), at least 1, and at most one split per two 64-row tiles
- * per wave.  mustafar_dense_decode_attn with splits = 0 uses the same rule with
+ * unit of an MI355X), at least 1, and at most ceil(tiles / 4) for the
+ * ceil(max_seq_len / 64) 64-row tiles (every wave gets at least one tile).
+ * mustafar_dense_decode_attn with splits = 0 uses the same rule with
  * 256 blocks (never more splits than this).  Host only.
  */
 int mustafar_decode_auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len);

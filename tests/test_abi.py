@@ -139,13 +139,14 @@ def test_workspace_sizing_and_auto_splits():
     # small sequences get one split; long single-sequence shapes get many
     assert L.mustafar_decode_auto_splits(1, 2, 256) == 1
     assert L.mustafar_decode_auto_splits(1, 32, 4096) >= 4
-    # the documented rule: floor(512 / units), at least 1, at most tiles / 8
+    # the documented rule: floor(512 / units), at least 1, at most ceil(tiles / 4)
     assert L.mustafar_decode_auto_splits(8, 8, 32768) == 8
     assert L.mustafar_decode_auto_splits(6, 8, 32768) == 10
     assert L.mustafar_decode_auto_splits(1, 8, 65536) == 64
     assert L.mustafar_decode_auto_splits(64, 8, 16384) == 1
     assert L.mustafar_decode_auto_splits(128, 8, 16384) == 1
-    assert L.mustafar_decode_auto_splits(1, 8, 1024) == 2  # 16 tiles: two per wave
+    assert L.mustafar_decode_auto_splits(1, 8, 1024) == 4  # 16 tiles: one per wave
+    assert L.mustafar_decode_auto_splits(1, 8, 4096) == 16
 
 
 def test_decode_argument_errors():

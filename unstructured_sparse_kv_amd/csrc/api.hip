@@ -85,13 +85,13 @@ int launched(hipError_t e) { return e == hipSuccess ? MUSTAFAR_OK : MUSTAFAR_ELA
 // Sequence splits per (batch, kv head) when the caller passes 0: as many 4-wave
 // blocks as fill the device once without a partial second round -- two per
 // compute unit for the sparse kernels (their LDS footprint allows two), one
-// for the dense kernel (measured fastest) -- with at least two 64-row tiles
+// for the dense kernel (measured fastest) -- with at least one 64-row tile
 // per wave.
 int auto_splits(int64_t batch, int64_t hkv, int64_t max_seq_len, int64_t target_blocks = 512) {
   const int64_t units = batch * hkv;
   const int64_t tiles = (max_seq_len + 63) / 64;
   int64_t s = target_blocks / units;
-  const int64_t most = (tiles + 2 * kDecodeWaves - 1) / (2 * kDecodeWaves);  // >= 2 tiles per wave
+  const int64_t most = (tiles + kDecodeWaves - 1) / kDecodeWaves;  // >= 1 tile per wave
   if (s > most) s = most;
   if (s < 1) s = 1;
   if (s > kMaxSplits) s = kMaxSplits;
