@@ -161,7 +161,7 @@ __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, uint32_t sta
 }
 
 // Chunks of 16 B covering n values starting at any half offset (+1 dword slack).
-__device__ __forceinline__ int row_chunks(int n) { return (((n + 1) >> 1) + 1 + 3) >> 2; }
+__host__ __device__ constexpr int row_chunks(int n) { return (((n + 1) >> 1) + 1 + 3) >> 2; }
 
 // Zeroes stored values beyond the first `count` of the row.  The masks come
 // from sign bits (all ones where the index is below count) rather than from
