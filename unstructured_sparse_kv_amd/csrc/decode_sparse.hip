@@ -104,9 +104,11 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
   const auto vbrs = make_rsrc(a.vbm + (int64_t)unit * a.cap * 2, (uint32_t)a.cap * 16u);
   const auto ktrs = make_rsrc(a.ktoff + (int64_t)unit * ntoff, (uint32_t)ntoff * 4u);
   const auto vtrs = make_rsrc(a.vtoff + (int64_t)unit * ntoff, (uint32_t)ntoff * 4u);
-  // chunks of each row's prefetch (a constant with an exact keep)
-  const int kch = NK > 0 ? row_chunks(NK) : row_chunks(kk);
-  const int vch = NK > 0 ? row_chunks(NK) : row_chunks(vk);
+  // chunks of each row's prefetch: a constant, so that no branch separates
+  // the loads (without an exact keep, the whole register budget: the extra
+  // bytes are the next rows' and hit the cache)
+  constexpr int kch = NK > 0 ? row_chunks(NK) : KW / 4;
+  constexpr int vch = kch;
   const bool k_odd = (kk & 1) != 0, v_odd = (vk & 1) != 0;
 
   // tile offsets of this wave's tiles, 64 at a time, one per lane
