@@ -39,6 +39,8 @@
 #include "merge.hpp"
 #include "select_row.hpp"
 
+#include <type_traits>
+
 namespace mustafar {
 namespace {
 
@@ -172,8 +174,9 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
                    const_cast<uint32_t*>(a.vtoff) + (int64_t)unit * ntoff, T_old,
                    new_lds + C::kNewSide);
   }
-  auto take_new = [&](int tile, const char* copy, uint4& bm, uint32_t (&row)[KW]) {
-    if (owner && tile == tile_new && lane == new_lane) {
+  // (only in the owner wave's last tile, which holds the new row: see the loop)
+  auto take_new = [&](const char* copy, uint4& bm, uint32_t (&row)[KW]) {
+    if (lane == new_lane) {
       bm = *reinterpret_cast<const uint4*>(copy);
 #pragma unroll
       for (int j = 0; j < KW; ++j) row[j] = reinterpret_cast<const uint32_t*>(copy + 16)[j];
@@ -232,7 +235,9 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
     *reinterpret_cast<uint16_t*>(smem + addr) = (uint16_t)vbits;
   };
 
-  for (int tile = tb; tile < te; ++tile) {
+  // One tile; PATCH (the owner wave's last tile) takes the new rows from LDS.
+  auto do_tile = [&](int tile, auto patch_tag) {
+    constexpr bool PATCH = decltype(patch_tag)::value;
     const int nvalid = min(kTile, T - tile * kTile);
     const bool valid = (int)lane < nvalid;
     const bool partial = nvalid < kTile;
@@ -241,10 +246,12 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
 
     // ---- key tile K[t][c]
     wave_lds_sync();  // the previous tile's reads (and clears) of the buffer are done
-    take_new(tile, new_lds, kb, krow);
+    if constexpr (PATCH) take_new(new_lds, kb, krow);
     decode_side<NMAX, NK, false, 2u>(krs, kt0, kk, valid, partial, !kEvenExact || !(kt0 & 1u), kb,
                                      krow, tile_base + lane * kKRow, 0u, scatter,
-                                     [&](uint32_t (&r)[KW]) { uint4 t; take_new(tile, new_lds, t, r); });
+                                     [&](uint32_t (&r)[KW]) {
+                                       if constexpr (PATCH) { uint4 t; take_new(new_lds, t, r); }
+                                     });
     issue_k(nxt, kt0n);
     wave_lds_sync();
 
@@ -312,11 +319,12 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
 
     // ---- value tile V[c][t] in the same buffer
     wave_lds_sync();  // score reads of the key tile done; p written
-    take_new(tile, new_lds + C::kNewSide, vb, vrow);
+    if constexpr (PATCH) take_new(new_lds + C::kNewSide, vb, vrow);
     decode_side<NMAX, NK, false, kVRow>(
         vrs, vt0, vk, valid, partial, !kEvenExact || !(vt0 & 1u), vb, vrow, tile_base + 2u * lane,
-        0u, scatter,
-        [&](uint32_t (&r)[KW]) { uint4 t; take_new(tile, new_lds + C::kNewSide, t, r); });
+        0u, scatter, [&](uint32_t (&r)[KW]) {
+          if constexpr (PATCH) { uint4 t; take_new(new_lds + C::kNewSide, t, r); }
+        });
     issue_v(nxt, vt0n);
     wave_lds_sync();
 
@@ -336,7 +344,12 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
     }
     kt0 = kt0n;
     vt0 = vt0n;
-  }
+  };
+  // The new row of a fused step is in the unit's last tile, the owner wave's
+  // last one (tile_new == te - 1); the other tiles run without the patch.
+  const int te_plain = owner ? te - 1 : te;
+  for (int tile = tb; tile < te_plain; ++tile) do_tile(tile, std::false_type{});
+  if (owner) do_tile(tile_new, std::true_type{});
 
   lsum += __shfl_xor(lsum, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
