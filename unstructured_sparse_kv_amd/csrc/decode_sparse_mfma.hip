@@ -235,12 +235,14 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
     *reinterpret_cast<uint16_t*>(smem + addr) = (uint16_t)vbits;
   };
 
-  // One tile; PATCH (the owner wave's last tile) takes the new rows from LDS.
-  auto do_tile = [&](int tile, auto patch_tag) {
+  // One tile.  Only the unit's last tile may end before its 64th row (TAIL);
+  // PATCH (the owner wave's last tile) takes the new rows from LDS.
+  auto do_tile = [&](int tile, auto patch_tag, auto tail_tag) {
     constexpr bool PATCH = decltype(patch_tag)::value;
-    const int nvalid = min(kTile, T - tile * kTile);
-    const bool valid = (int)lane < nvalid;
-    const bool partial = nvalid < kTile;
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const int nvalid = TAIL ? min(kTile, T - tile * kTile) : kTile;
+    const bool valid = TAIL ? (int)lane < nvalid : true;
+    const bool partial = TAIL && nvalid < kTile;
     const int nxt = min(tile + 1, te - 1);
     offsets(nxt, kt0n, vt0n);
 
@@ -345,11 +347,18 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
     kt0 = kt0n;
     vt0 = vt0n;
   };
-  // The new row of a fused step is in the unit's last tile, the owner wave's
-  // last one (tile_new == te - 1); the other tiles run without the patch.
-  const int te_plain = owner ? te - 1 : te;
-  for (int tile = tb; tile < te_plain; ++tile) do_tile(tile, std::false_type{});
-  if (owner) do_tile(tile_new, std::true_type{});
+  // The unit's last tile (which holds a fused step's new row, tile_new ==
+  // te - 1 in the owner wave) runs on its own; the others need neither the
+  // tail masks nor the patch.
+  const bool has_last = tb < te && te == ntiles;
+  const int te_plain = has_last ? te - 1 : te;
+  for (int tile = tb; tile < te_plain; ++tile) do_tile(tile, std::false_type{}, std::false_type{});
+  if (has_last) {
+    if (owner)
+      do_tile(te - 1, std::true_type{}, std::true_type{});
+    else
+      do_tile(te - 1, std::false_type{}, std::true_type{});
+  }
 
   lsum += __shfl_xor(lsum, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
