@@ -17,8 +17,10 @@ constexpr int kWavesPerBlock = kPruneBlock / kWave;
 constexpr int kRowsPerWave = kTile / kWavesPerBlock;  // 16
 
 // Grid (64-row tiles, units); wave w of a block prunes rows
-// tile * 64 + 16w .. + 15 of its (batch, kv head) unit, one row at a time with
-// the next row's loads in flight.  Units beyond gridDim.y are taken in steps
+// tile * 64 + 16w .. + 15 of its (batch, kv head) unit.  All 16 rows are
+// loaded before the first is pruned: a row's selection takes far less time
+// than a load's latency, so a wave that waited for each row in turn would
+// spend most of its time stalled.  Units beyond gridDim.y are taken in steps
 // of gridDim.y.  Row indices stay 32-bit within a unit.  Head h of a unit keeps
 // keep_of(map, h) values per row.
 // TWO_FOUR: the 2:4 comparator rule instead of the per-token top-keep rule
@@ -43,22 +45,24 @@ __global__ __launch_bounds__(kPruneBlock) void prune_compress_kernel(PruneArgs a
     const uint16_t* src = a.dense + ((int64_t)unit * a.t_stride + t0) * kHeadDim;
     uint64_t* bm = a.bitmaps + ((int64_t)unit * a.cap + t0) * 2;
     uint16_t* vals = a.values + region_of(a.map, kMapAt, b, h, a.cap) + (int64_t)t0 * keep;
-    uint32_t x0 = src[lane], x1 = src[lane + 64];
-    for (int t = t0; t < tend; ++t) {
-      // next row's loads (the last row reloads itself)
-      const int64_t step = (t + 1 < tend) ? kHeadDim : 0;
-      const uint32_t y0 = src[step + lane], y1 = src[step + lane + 64];
-      const RowMask m = TWO_FOUR ? select_row_24(x0, x1) : select_row(x0, x1, keep);
-      store_row(m, x0, x1, bm, vals);
+    const int n = tend - t0;  // 1 .. 16 rows
+    uint32_t x0[kRowsPerWave], x1[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int r = i < n ? i : n - 1;  // rows past the end load the last one again
+      x0[i] = src[r * kHeadDim + lane];
+      x1[i] = src[r * kHeadDim + lane + 64];
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      if (i >= n) break;
+      const int t = t0 + i;
+      const RowMask m = TWO_FOUR ? select_row_24(x0[i], x1[i]) : select_row(x0[i], x1[i], keep);
+      store_row(m, x0[i], x1[i], bm + 2 * i, vals + (int64_t)i * keep);
       if (lane == 0) {
         if (t % kTile == 0) toff[t / kTile] = (uint32_t)(t * keep);
         if (t == T - 1) toff[(T + kTile - 1) / kTile] = (uint32_t)(T * keep);
       }
-      src += step;
-      bm += 2;
-      vals += keep;
-      x0 = y0;
-      x1 = y1;
     }
   }
 }
