@@ -466,3 +466,65 @@ def test_edge_cases(gpu):
     assert full.cpu().tolist() == [cap] * 4
     for a, b in zip(before, kc.views()):
         assert torch.equal(a, b)
+
+
+def test_shared_workspace_across_shapes(gpu):
+    """One workspace serves a run of calls of different shapes, split counts and
+    kernels (sparse, vector-unit, dense, fused step): whatever earlier calls left
+    in it, each output must match the same call on a fresh workspace bit for bit,
+    and the oracle; the fused step advances every length exactly once."""
+    ws = usk.make_workspace(8, 32, 8, 4096, splits=64, device=gpu)
+    cases = [  # (B, Hq, Hkv, T, keep, splits, kernel)
+        (3, 8, 2, 300, 38, 0, "mfma"), (3, 8, 2, 300, 38, 5, "mfma"), (1, 4, 4, 1000, 64, 0, "mfma"),
+        (4, 32, 8, 200, 38, 3, "valu"), (2, 2, 2, 130, 13, 7, "mfma"), (3, 8, 2, 300, 38, 0, "mfma"),
+        (2, 16, 2, 700, 38, 0, "dense"), (3, 8, 2, 300, 38, 5, "step"), (3, 8, 2, 300, 38, 5, "step"),
+        (2, 8, 1, 257, 64, 64, "mfma"), (3, 8, 2, 300, 38, 0, "mfma")]
+    for i, (B, Hq, Hkv, T, keep, splits, kern) in enumerate(cases):
+        say(f"shared workspace call {i}: B={B} Hq={Hq} Hkv={Hkv} T={T} keep={keep} splits={splits} {kern}")
+        K, V, q = _small_inputs(B, Hq, Hkv, T + 1, 7000 + i)
+        cap = (T // 64 + 2) * 64  # room for the appended row
+        seq = np.array([T - 17 * b for b in range(B)], np.int32)
+        qd = q.to(gpu)
+        out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float16, device=gpu)
+        fresh = torch.full_like(out, float("nan"))
+        if kern == "dense":
+            Kd, Vd, sd = K[:, :, :T].contiguous().to(gpu), V[:, :, :T].contiguous().to(gpu), torch.from_numpy(seq).to(gpu)
+            usk.dense_decode_attn(qd, Kd, Vd, sd, T, SCALE, out, ws, splits)
+            usk.dense_decode_attn(qd, Kd, Vd, sd, T, SCALE, fresh,
+                                  usk.make_workspace(B, Hq, Hkv, T, splits, device=gpu), splits)
+            torch.cuda.synchronize()
+            ref = oracle.attention_dense(q, K[:, :, :T].contiguous(), V[:, :, :T].contiguous(), seq, SCALE)
+        elif kern == "step":
+            outs = []
+            for w in (ws, usk.make_workspace(B, Hq, Hkv, T + 1, splits, device=gpu)):
+                sd = torch.from_numpy(seq).to(gpu)
+                kc = compress_on_gpu(K.to(gpu), sd, keep, cap)
+                vc = compress_on_gpu(V.to(gpu), sd, keep, cap)
+                kn = K[:, :, T].contiguous().to(gpu)
+                vn = V[:, :, T].contiguous().to(gpu)
+                o = out if w is ws else fresh
+                usk.decode_step(qd, kc, vc, kn, vn, sd, T + 1, SCALE, o, w, splits=splits)
+                torch.cuda.synchronize()
+                assert np.array_equal(sd.cpu().numpy(), seq + 1), "seq_lens not advanced exactly once"
+                outs.append((kc, vc))
+            # the reference: the caches after the step, attended over seq + 1 rows
+            Kr = K.clone()
+            Vr = V.clone()
+            for b in range(B):  # the new row sits at seq[b]
+                Kr[b, :, seq[b]] = K[b, :, T]
+                Vr[b, :, seq[b]] = V[b, :, T]
+            ko = oracle.compress(Kr, seq + 1, keep, cap)
+            vo = oracle.compress(Vr, seq + 1, keep, cap)
+            ref = oracle.attention_compressed(q, ko, vo, seq + 1, SCALE)
+        else:
+            sd = torch.from_numpy(seq).to(gpu)
+            kc = compress_on_gpu(K.to(gpu), sd, keep, cap)
+            vc = compress_on_gpu(V.to(gpu), sd, keep, cap)
+            SPARSE[kern](qd, kc, vc, sd, T, SCALE, out, ws, splits)
+            SPARSE[kern](qd, kc, vc, sd, T, SCALE, fresh,
+                         usk.make_workspace(B, Hq, Hkv, T, splits, device=gpu), splits)
+            torch.cuda.synchronize()
+            ref = oracle.attention_compressed(q, oracle.compress(K, seq, keep, cap),
+                                              oracle.compress(V, seq, keep, cap), seq, SCALE)
+        assert np.array_equal(u16(out), u16(fresh)), f"call {i}: shared and fresh workspace differ"
+        assert_attn_close(_f64(out), ref, f"shared workspace call {i} ({kern})")
