@@ -53,15 +53,18 @@ __global__ __launch_bounds__(kPruneBlock) void prune_compress_kernel(PruneArgs a
       x0[i] = src[r * kHeadDim + lane];
       x1[i] = src[r * kHeadDim + lane + 64];
     }
+    // unrolled (each row under a uniform test) so that the rows stay in fixed
+    // registers and their addresses are constant offsets
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
-      if (i >= n) break;
-      const int t = t0 + i;
-      const RowMask m = TWO_FOUR ? select_row_24(x0[i], x1[i]) : select_row(x0[i], x1[i], keep);
-      store_row(m, x0[i], x1[i], bm + 2 * i, vals + (int64_t)i * keep);
-      if (lane == 0) {
-        if (t % kTile == 0) toff[t / kTile] = (uint32_t)(t * keep);
-        if (t == T - 1) toff[(T + kTile - 1) / kTile] = (uint32_t)(T * keep);
+      if (i < n) {
+        const int t = t0 + i;
+        const RowMask m = TWO_FOUR ? select_row_24(x0[i], x1[i]) : select_row(x0[i], x1[i], keep);
+        store_row(m, x0[i], x1[i], bm + 2 * i, vals + (int64_t)i * keep);
+        if (lane == 0) {
+          if (t % kTile == 0) toff[t / kTile] = (uint32_t)(t * keep);
+          if (t == T - 1) toff[(T + kTile - 1) / kTile] = (uint32_t)(T * keep);
+        }
       }
     }
   }

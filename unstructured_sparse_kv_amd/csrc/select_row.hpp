@@ -19,8 +19,10 @@ struct RowMask {
 // Survivors of one row: the `keep` largest magnitude keys (bits & 0x7FFF; finite
 // fp16 magnitudes order like these integers, and -0 == +0), ties to the lower
 // channel.  tau is found by an MSB-first bisection over the 15 key bits: the
-// largest value with #(key >= tau) >= keep, i.e. the keep-th largest key.  The
-// loop stops early once exactly `keep` keys are >= the candidate.
+// largest value with #(key >= tau) >= keep, i.e. the keep-th largest key.  From
+// bit 10 down the loop stops early once exactly `keep` keys are >= the
+// candidate (any such candidate selects the same survivors); above it an exact
+// count is too rare to be worth the test's scalar instructions.
 __device__ __forceinline__ RowMask select_row(uint32_t x0, uint32_t x1, int keep) {
   const uint32_t k0 = x0 & 0x7FFFu, k1 = x1 & 0x7FFFu;
   uint32_t tau = 0;
@@ -29,7 +31,7 @@ __device__ __forceinline__ RowMask select_row(uint32_t x0, uint32_t x1, int keep
     const uint32_t cand = tau | (1u << b);
     const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
     if (cnt >= keep) tau = cand;
-    if (cnt == keep) break;
+    if (b <= 10 && cnt == keep) break;
   }
   const uint64_t g0 = __ballot(k0 > tau), g1 = __ballot(k1 > tau);
   const int need = keep - (__popcll(g0) + __popcll(g1));
