@@ -528,3 +528,30 @@ def test_shared_workspace_across_shapes(gpu):
                                               oracle.compress(V, seq, keep, cap), seq, SCALE)
         assert np.array_equal(u16(out), u16(fresh)), f"call {i}: shared and fresh workspace differ"
         assert_attn_close(_f64(out), ref, f"shared workspace call {i} ({kern})")
+
+
+def test_prune_exact_count_at_high_key_bits(gpu):
+    """Rows whose keep-th and (keep+1)-th largest magnitudes first differ at key
+    bit 14, 13, 12, 11 or 10, so that a candidate with exactly keep keys at or
+    above it appears at that bit of the MSB-first search: the survivors must be
+    the oracle's whatever bit the search stops at."""
+    rng = np.random.default_rng(4242)
+    rows = []
+    for keep in (1, 38, 64, 127):
+        for bit in (14, 13, 12, 11, 10):
+            for _ in range(4):
+                hi_key = (1 << bit) | int(rng.integers(0, 1 << bit))  # top bit `bit` set
+                lo_key = int(rng.integers(0, 1 << bit))               # below 1 << bit
+                keys = np.concatenate([np.full(keep, hi_key), rng.integers(0, lo_key + 1, 128 - keep)])
+                keys = np.minimum(keys, 0x7BFF)  # finite fp16 magnitudes
+                sign = rng.integers(0, 2, 128) << 15
+                rows.append((keys | sign)[rng.permutation(128)].astype(np.uint16))
+    x = np.stack(rows).view(np.int16).reshape(1, 1, -1, 128)
+    seq = np.array([x.shape[2]], np.int32)
+    cap = (x.shape[2] + 63) // 64 * 64
+    xt = torch.from_numpy(x.copy())
+    for keep in (1, 38, 64, 127):
+        say(f"high-bit exact counts keep={keep}")
+        c = compress_on_gpu(xt.to(gpu), torch.from_numpy(seq).to(gpu), keep, cap)
+        torch.cuda.synchronize()
+        assert_compressed_equal(c, oracle.compress(xt, seq, keep, cap), seq)
