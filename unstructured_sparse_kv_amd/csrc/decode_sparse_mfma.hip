@@ -51,6 +51,13 @@ constexpr uint32_t kKRow = 272;  // key tile row: 128 fp16 + 16 B (general-walk 
 constexpr uint32_t kVRow = 144;  // value tile channel row: 64 fp16 + 16 B
 // value tile + the general walk's dump row (channel 128); the key tile (64 x 272) fits too
 constexpr int kTileBytes = 129 * 144;
+
+// v within each 16-lane row rotated by N lanes (DPP row_ror:N)
+template <int N>
+__device__ __forceinline__ float row_ror_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xF,
+                                                            0xF, false));
+}
 constexpr float kRescaleSlack = 8.f;   // log2 units
 
 template <int G, int KW>
@@ -271,6 +278,50 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
       }
     }
 
+    if constexpr (G <= 4) {
+      // ---- online softmax, compacted: block mb's scores of head h move to
+      // lane 4 mb + h of each 16-lane row (the lanes of heads >= 4 held no
+      // scores), so every lane holds 4: head l16 % 4, tile rows
+      // 16 (l16 / 4) + 4 grp + i (log2 units)
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // (vector elements copied out first: a bit cast applied to cs[mb][i]
+        // directly compiles to element 0 for every i)
+        const float e0 = cs[0][i], e1 = cs[1][i], e2 = cs[2][i], e3 = cs[3][i];
+        int r = __builtin_bit_cast(int, e0);
+        r = __builtin_amdgcn_update_dpp(r, __builtin_bit_cast(int, e1), 0x114, 0xF, 0x2, false);
+        r = __builtin_amdgcn_update_dpp(r, __builtin_bit_cast(int, e2), 0x118, 0xF, 0x4, false);
+        r = __builtin_amdgcn_update_dpp(r, __builtin_bit_cast(int, e3), 0x11C, 0xF, 0x8, false);
+        sv[i] = __builtin_bit_cast(float, r) * a.scale_log2;
+      }
+      const int row0 = 16 * (int)(l16 >> 2) + 4 * (int)grp;
+      if (partial) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = (row0 + i < nvalid) ? sv[i] : ninf;
+      }
+      float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mt = fmaxf(mt, row_ror_f<4>(mt));
+      mt = fmaxf(mt, row_ror_f<8>(mt));
+      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      // m, lsum: head l16 % 4 (lanes l16 < G hold the heads' states proper)
+      if (__ballot(mt > m + kRescaleSlack) != 0ull) {
+        const float mn = fmaxf(m, mt);
+        const float alpha = exp2_raw(m - mn);
+        m = mn;
+        lsum *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
+      }
+      const float p0 = exp2_raw(sv[0] - m), p1 = exp2_raw(sv[1] - m);
+      const float p2 = exp2_raw(sv[2] - m), p3 = exp2_raw(sv[3] - m);
+      lsum += (p0 + p1) + (p2 + p3);
+      if ((int)(l16 & 3u) < G)
+        *reinterpret_cast<uint2*>(p_lds + (l16 & 3u) * 64 + row0) = make_uint2(
+            (uint32_t)float_to_half_bits(p0) | ((uint32_t)float_to_half_bits(p1) << 16),
+            (uint32_t)float_to_half_bits(p2) | ((uint32_t)float_to_half_bits(p3) << 16));
+    } else {
     // ---- online softmax for head l16 (log2 units)
     float sv[16];
 #pragma unroll
@@ -318,6 +369,7 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
         *reinterpret_cast<uint2*>(p_lds + l16 * 64 + 16 * mb + 4 * grp) =
             make_uint2(ph[2 * mb], ph[2 * mb + 1]);
     }
+    }
 
     // ---- value tile V[c][t] in the same buffer
     wave_lds_sync();  // score reads of the key tile done; p written
@@ -360,6 +412,10 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
       do_tile(te - 1, std::false_type{}, std::true_type{});
   }
 
+  if constexpr (G <= 4) {  // the compacted layout spreads a head's sum over 4 lanes of each row
+    lsum += row_ror_f<4>(lsum);
+    lsum += row_ror_f<8>(lsum);
+  }
   lsum += __shfl_xor(lsum, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
   __syncthreads();  // the merge area overlaps the per-wave buffers
