@@ -50,7 +50,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "sparse decode-attn GB/s (% HBM peak) + speedup vs dense fp16, Llama-3-8B shape 70%"
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the timed decode call (split kernel, its helpers, the merge kernel, the launcher)
-DECODE_SOURCES = ["decode_sparse_mfma.hip", "decode_walk.hpp", "merge.hpp", "device_common.hpp",
+DECODE_SOURCES = ["decode_sparse_mfma.hip", "decode_walk.hpp", "merge.hpp", "tile_softmax.hpp", "device_common.hpp",
                   "kernels.hpp", "select_row.hpp", "util.hip", "api.hip"]
 DECODE_KERNELS = "decode_sparse_mfma_kernel<4,40,38> + decode_reduce_kernel"
 

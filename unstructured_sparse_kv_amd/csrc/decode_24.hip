@@ -32,6 +32,7 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "merge.hpp"
+#include "tile_softmax.hpp"
 
 namespace mustafar {
 namespace {
@@ -44,7 +45,6 @@ typedef __attribute__((address_space(3))) short4v lds_short4;
 constexpr int kRowBytes = 2 * kHeadDim;        // one dense row
 constexpr int kTile24 = kTile * kRowBytes;     // 64 dense rows: the key tile, then the value tile
 constexpr int kGroups = kHeadDim / 4;          // 32 groups of 4 channels per row
-constexpr float kSlack = 8.f;                  // log2 units
 
 template <int G>
 struct Cfg24 {
@@ -117,7 +117,7 @@ void decode_24_kernel(SparseDecodeArgs a) {
   }
 
   const float ninf = -__builtin_inff();
-  float m = ninf, lsum = 0.f;  // head l16
+  float m = ninf, lsum = 0.f;  // softmax state (tile_softmax.hpp)
   floatx4 acc[8];              // out[channel 16*mb + 4*grp + i][head l16]
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -202,50 +202,8 @@ void decode_24_kernel(SparseDecodeArgs a) {
       }
     }
 
-    // ---- online softmax for head l16 (log2 units)
-    float sv[16];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[4 * mb + i] = cs[mb][i] * a.scale_log2;
-    if (partial) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sv[4 * mb + i] = (16 * mb + 4 * (int)grp + i < nvalid) ? sv[4 * mb + i] : ninf;
-    }
-    float mt = ninf;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sv[j]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    if (__ballot(mt > m + kSlack) != 0ull) {
-      const float mn = fmaxf(m, mt);
-      const float alpha = exp2_raw(m - mn);
-      m = mn;
-      lsum *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
-    }
-    const float mn = m;
-    float ps = 0.f;
-    uint32_t ph[8];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const float p0 = exp2_raw(sv[4 * mb + 0] - mn), p1 = exp2_raw(sv[4 * mb + 1] - mn);
-      const float p2 = exp2_raw(sv[4 * mb + 2] - mn), p3 = exp2_raw(sv[4 * mb + 3] - mn);
-      ps += (p0 + p1) + (p2 + p3);
-      ph[2 * mb] = (uint32_t)float_to_half_bits(p0) | ((uint32_t)float_to_half_bits(p1) << 16);
-      ph[2 * mb + 1] = (uint32_t)float_to_half_bits(p2) | ((uint32_t)float_to_half_bits(p3) << 16);
-    }
-    lsum += ps;
-    if ((int)l16 < G) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        *reinterpret_cast<uint2*>(p_lds + l16 * 64 + 16 * mb + 4 * grp) =
-            make_uint2(ph[2 * mb], ph[2 * mb + 1]);
-    }
+    // ---- online softmax (tile_softmax.hpp); p to LDS
+    tile_softmax<G>(cs, a.scale_log2, partial, nvalid, l16, grp, m, lsum, acc, p_lds);
 
     // ---- value tile in the same buffer
     wave_lds_sync();  // score reads of the key tile done; p written
@@ -279,8 +237,7 @@ void decode_24_kernel(SparseDecodeArgs a) {
     }
   }
 
-  lsum += __shfl_xor(lsum, 16, kWave);
-  lsum += __shfl_xor(lsum, 32, kWave);
+  lsum = tile_softmax_sum<G>(lsum);
   __syncthreads();  // the merge area overlaps the per-wave buffers
   float* lds_m = reinterpret_cast<float*>(smem);
   float* lds_l = lds_m + kDecodeWaves * G;

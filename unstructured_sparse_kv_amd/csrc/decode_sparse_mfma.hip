@@ -37,6 +37,7 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "merge.hpp"
+#include "tile_softmax.hpp"
 #include "select_row.hpp"
 
 #include <type_traits>
@@ -52,13 +53,6 @@ constexpr uint32_t kVRow = 144;  // value tile channel row: 64 fp16 + 16 B
 // value tile + the general walk's dump row (channel 128); the key tile (64 x 272) fits too
 constexpr int kTileBytes = 129 * 144;
 
-// v within each 16-lane row rotated by N lanes (DPP row_ror:N)
-template <int N>
-__device__ __forceinline__ float row_ror_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xF,
-                                                            0xF, false));
-}
-constexpr float kRescaleSlack = 8.f;   // log2 units
 
 template <int G, int KW>
 struct MfmaCfg {
@@ -137,7 +131,7 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
   }
 
   const float ninf = -__builtin_inff();
-  float m = ninf, lsum = 0.f;  // head l16
+  float m = ninf, lsum = 0.f;  // softmax state (tile_softmax.hpp)
   floatx4 acc[8];              // out[channel 16*mb + 4*grp + i][head l16]
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -278,98 +272,8 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
       }
     }
 
-    if constexpr (G <= 4) {
-      // ---- online softmax, compacted: block mb's scores of head h move to
-      // lane 4 mb + h of each 16-lane row (the lanes of heads >= 4 held no
-      // scores), so every lane holds 4: head l16 % 4, tile rows
-      // 16 (l16 / 4) + 4 grp + i (log2 units)
-      float sv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // (vector elements copied out first: a bit cast applied to cs[mb][i]
-        // directly compiles to element 0 for every i)
-        const float e0 = cs[0][i], e1 = cs[1][i], e2 = cs[2][i], e3 = cs[3][i];
-        int r = __builtin_bit_cast(int, e0);
-        r = __builtin_amdgcn_update_dpp(r, __builtin_bit_cast(int, e1), 0x114, 0xF, 0x2, false);
-        r = __builtin_amdgcn_update_dpp(r, __builtin_bit_cast(int, e2), 0x118, 0xF, 0x4, false);
-        r = __builtin_amdgcn_update_dpp(r, __builtin_bit_cast(int, e3), 0x11C, 0xF, 0x8, false);
-        sv[i] = __builtin_bit_cast(float, r) * a.scale_log2;
-      }
-      const int row0 = 16 * (int)(l16 >> 2) + 4 * (int)grp;
-      if (partial) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[i] = (row0 + i < nvalid) ? sv[i] : ninf;
-      }
-      float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mt = fmaxf(mt, row_ror_f<4>(mt));
-      mt = fmaxf(mt, row_ror_f<8>(mt));
-      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-      // m, lsum: head l16 % 4 (lanes l16 < G hold the heads' states proper)
-      if (__ballot(mt > m + kRescaleSlack) != 0ull) {
-        const float mn = fmaxf(m, mt);
-        const float alpha = exp2_raw(m - mn);
-        m = mn;
-        lsum *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
-      }
-      const float p0 = exp2_raw(sv[0] - m), p1 = exp2_raw(sv[1] - m);
-      const float p2 = exp2_raw(sv[2] - m), p3 = exp2_raw(sv[3] - m);
-      lsum += (p0 + p1) + (p2 + p3);
-      if ((int)(l16 & 3u) < G)
-        *reinterpret_cast<uint2*>(p_lds + (l16 & 3u) * 64 + row0) = make_uint2(
-            (uint32_t)float_to_half_bits(p0) | ((uint32_t)float_to_half_bits(p1) << 16),
-            (uint32_t)float_to_half_bits(p2) | ((uint32_t)float_to_half_bits(p3) << 16));
-    } else {
-    // ---- online softmax for head l16 (log2 units)
-    float sv[16];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[4 * mb + i] = cs[mb][i] * a.scale_log2;
-    if (partial) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sv[4 * mb + i] = (16 * mb + 4 * (int)grp + i < nvalid) ? sv[4 * mb + i] : ninf;
-    }
-    float mt = ninf;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sv[j]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    // The reference m moves only when a score exceeds it by more than
-    // kRescaleSlack, so p stays below 2^kRescaleSlack (well inside the fp16
-    // range, same relative precision); most tiles skip the rescale.
-    if (__ballot(mt > m + kRescaleSlack) != 0ull) {
-      const float mn = fmaxf(m, mt);
-      const float alpha = exp2_raw(m - mn);
-      m = mn;
-      lsum *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
-    }
-    const float mn = m;
-    float ps = 0.f;
-    uint32_t ph[8];  // fp16 pairs for p_lds
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const float p0 = exp2_raw(sv[4 * mb + 0] - mn), p1 = exp2_raw(sv[4 * mb + 1] - mn);
-      const float p2 = exp2_raw(sv[4 * mb + 2] - mn), p3 = exp2_raw(sv[4 * mb + 3] - mn);
-      ps += (p0 + p1) + (p2 + p3);
-      ph[2 * mb] = (uint32_t)float_to_half_bits(p0) | ((uint32_t)float_to_half_bits(p1) << 16);
-      ph[2 * mb + 1] = (uint32_t)float_to_half_bits(p2) | ((uint32_t)float_to_half_bits(p3) << 16);
-    }
-    lsum += ps;
-    if ((int)l16 < G) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        *reinterpret_cast<uint2*>(p_lds + l16 * 64 + 16 * mb + 4 * grp) =
-            make_uint2(ph[2 * mb], ph[2 * mb + 1]);
-    }
-    }
+    // ---- online softmax (tile_softmax.hpp); p to LDS
+    tile_softmax<G>(cs, a.scale_log2, partial, nvalid, l16, grp, m, lsum, acc, p_lds);
 
     // ---- value tile V[c][t] in the same buffer
     wave_lds_sync();  // score reads of the key tile done; p written
@@ -412,12 +316,7 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
       do_tile(te - 1, std::false_type{}, std::true_type{});
   }
 
-  if constexpr (G <= 4) {  // the compacted layout spreads a head's sum over 4 lanes of each row
-    lsum += row_ror_f<4>(lsum);
-    lsum += row_ror_f<8>(lsum);
-  }
-  lsum += __shfl_xor(lsum, 16, kWave);
-  lsum += __shfl_xor(lsum, 32, kWave);
+  lsum = tile_softmax_sum<G>(lsum);
   __syncthreads();  // the merge area overlaps the per-wave buffers
   float* lds_m = reinterpret_cast<float*>(smem);
   float* lds_l = lds_m + kDecodeWaves * G;
