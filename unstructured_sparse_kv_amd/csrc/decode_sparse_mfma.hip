@@ -17,11 +17,11 @@
 //               from LDS, B = the G query heads as columns (registers), 4 row
 //               blocks x 4 channel blocks; lane l ends with head l%16 of rows
 //               16*mb + 4*(l/16) + i.
-//   softmax     per head: max over the lane's 16 rows and across the 4 lane
-//               groups; the running reference max is raised (and the
-//               accumulators rescaled) only when a score exceeds it by more
-//               than 8 in log2 units, so p <= 2^8; exp2, running sums; p to
-//               LDS as fp16 p[head][row].
+//   softmax     tile_softmax.hpp: per head, online; with G <= 4 the scores
+//               are first compacted onto the lanes of the padding heads; the
+//               running reference max is raised (and the accumulators
+//               rescaled) only when a score exceeds it by more than 8 in log2
+//               units, so p <= 2^8; p to LDS as fp16 p[head][row].
 //   value tile  walk the value bitmap into a zeroed channel-major tile
 //               V[c][t] in the same LDS buffer (row stride 144 B).
 //   P.V         v_mfma_f32_16x16x32_f16: A = 16 channels x 32 rows of V,
