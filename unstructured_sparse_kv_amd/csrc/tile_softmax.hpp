@@ -15,7 +15,9 @@
 // real scores (head l16 % 4, rows 16 (l16 / 4) + 4 grp + i) instead of 16 of
 // which most are padding; the scaling, exponentials and conversions then run a
 // quarter as often.  A head's maximum and sum are gathered over the four banks
-// with row_ror 4 and 8 and over the lane groups with xor 16 and 32.
+// with row_ror 4 and 8 and over the lane groups with xor 16 and 32.  With G = 8
+// the same is done with one move per register (blocks 2 and 3 to the lanes of
+// columns 8-15), leaving 8 scores per lane.
 #pragma once
 
 #include "device_common.hpp"
@@ -80,6 +82,56 @@ __device__ __forceinline__ void tile_softmax(const f32x4 (&cs)[4], float scale_l
       *reinterpret_cast<uint2*>(p_lds + (l16 & 3u) * 64 + row0) = make_uint2(
           (uint32_t)float_to_half_bits(p0) | ((uint32_t)float_to_half_bits(p1) << 16),
           (uint32_t)float_to_half_bits(p2) | ((uint32_t)float_to_half_bits(p3) << 16));
+  } else if constexpr (G == 8) {
+    // heads in columns 0-7: blocks 2 and 3 move to the lanes of columns 8-15,
+    // so lane l16 holds head l16 % 8, row blocks 2 (l16 / 8) and 2 (l16 / 8) + 1
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e0 = cs[0][i], e1 = cs[1][i], e2 = cs[2][i], e3 = cs[3][i];
+      sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                  __builtin_bit_cast(int, e0), __builtin_bit_cast(int, e2), 0x118, 0xF, 0xC, false)) *
+              scale_log2;
+      sv[4 + i] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                      __builtin_bit_cast(int, e1), __builtin_bit_cast(int, e3), 0x118, 0xF, 0xC, false)) *
+                  scale_log2;
+    }
+    const int row0 = 32 * (int)(l16 >> 3) + 4 * (int)grp;  // rows row0 + i and row0 + 16 + i
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = (row0 + i < nvalid) ? sv[i] : ninf;
+        sv[4 + i] = (row0 + 16 + i < nvalid) ? sv[4 + i] : ninf;
+      }
+    }
+    float mt = ninf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mt = fmaxf(mt, sv[j]);
+    mt = fmaxf(mt, row_ror_f<8>(mt));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    if (__ballot(mt > m + kSoftmaxSlack) != 0ull) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = exp2_raw(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) acc[mb] *= alpha;
+    }
+    float ps = 0.f;
+    uint32_t ph[4];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float p0 = exp2_raw(sv[4 * hb + 0] - m), p1 = exp2_raw(sv[4 * hb + 1] - m);
+      const float p2 = exp2_raw(sv[4 * hb + 2] - m), p3 = exp2_raw(sv[4 * hb + 3] - m);
+      ps += (p0 + p1) + (p2 + p3);
+      ph[2 * hb] = (uint32_t)float_to_half_bits(p0) | ((uint32_t)float_to_half_bits(p1) << 16);
+      ph[2 * hb + 1] = (uint32_t)float_to_half_bits(p2) | ((uint32_t)float_to_half_bits(p3) << 16);
+    }
+    lsum += ps;
+    uint16_t* pr = p_lds + (l16 & 7u) * 64 + row0;
+    *reinterpret_cast<uint2*>(pr) = make_uint2(ph[0], ph[1]);
+    *reinterpret_cast<uint2*>(pr + 16) = make_uint2(ph[2], ph[3]);
   } else {
     float sv[16];
 #pragma unroll
@@ -131,6 +183,8 @@ template <int G>
 __device__ __forceinline__ float tile_softmax_sum(float lsum) {
   if constexpr (G <= 4) {
     lsum += row_ror_f<4>(lsum);
+    lsum += row_ror_f<8>(lsum);
+  } else if constexpr (G == 8) {
     lsum += row_ror_f<8>(lsum);
   }
   lsum += __shfl_xor(lsum, 16, kWave);
