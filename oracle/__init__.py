@@ -77,6 +77,8 @@ def lib():
         L.orc_decompress_hk.argtypes = [P, P, P, Ci, Ci, I64, Ci, Ci, P, P, P]
         L.orc_used_bytes_hk.restype = I64
         L.orc_used_bytes_hk.argtypes = [Ci, Ci, P, I64, Ci, Ci, P]
+        L.orc_append_rows.restype = Ci
+        L.orc_append_rows.argtypes = [P, P, P, Ci, Ci, I64, Ci, Ci, P, P, P, P]
         L.orc_attention_compressed_hk.restype = Ci
         L.orc_attention_compressed_hk.argtypes = [P, Ci, Ci, Ci, Ci, P, P, P, Ci, P, P, P, P, Ci, P,
                                                   I64, P, F64, P, I64, P, Ci]
@@ -202,6 +204,31 @@ def compress(dense, seq_lens, k: int, cap: int | None = None, nthreads: int = 0,
     if rc != 0:
         raise ValueError("orc_compress: bad arguments")
     return c
+
+
+def append_rows(c: Compressed, rows, seq_lens) -> int:
+    """Appends one new row per (b, h) (rows: [B][H][d] fp16) to `c` in place at row
+    seq_lens[b], pruned per token (the oracle's append rule).  seq_lens is not changed.
+    Returns the status bits (1: some sequence was already at capacity)."""
+    x = _u16(rows)
+    assert x.shape == (c.B, c.H, c.d), x.shape
+    seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    st = np.zeros(1, dtype=np.uint32)
+    rc = lib().orc_append_rows(_p(c.bitmaps), _p(c.values), _p(c.tile_off), c.B, c.H, c.cap, c.d,
+                               c.k, c._hk(), _p(x), _p(seq), _p(st))
+    if rc != 0:
+        raise ValueError("orc_append_rows: bad arguments")
+    return int(st[0])
+
+
+def append_step(kc: Compressed, vc: Compressed, k_new, v_new, seq_lens) -> tuple:
+    """One decode-time append to both caches: the new key and value rows are appended
+    at seq_lens[b]; returns (new seq_lens, status).  A sequence at capacity keeps its
+    length and sets status bit 0."""
+    seq = np.asarray(seq_lens, dtype=np.int32)
+    st = append_rows(kc, k_new, seq) | append_rows(vc, v_new, seq)
+    grown = np.where(np.clip(seq, 0, kc.cap) < kc.cap, np.clip(seq, 0, kc.cap) + 1, np.clip(seq, 0, kc.cap))
+    return grown.astype(np.int32), st
 
 
 def decompress(c: Compressed, seq_lens) -> np.ndarray:

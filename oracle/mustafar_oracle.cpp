@@ -314,6 +314,59 @@ int orc_compress_24(const uint16_t* dense, int B, int H, int64_t t_stride, int d
                        tile_off, nthreads, true);
 }
 
+// Decode-time append of one new row per (b, h) to a compressed tensor
+// ([Summary] "Approach" and [Abstract]: the tokens produced during decode are
+// pruned and compressed at run time; R10: the new row is stored before the
+// step's attention reads the cache).  The new row of (b, h) is rows[(b*H + h)*d ..]:
+//   - it is pruned per token to keep (kept channels of that head, R22) by the
+//     rule of prune_row, whatever rule wrote the rows before it (channel-wise
+//     caches grow by per-token rows, R24);
+//   - it becomes row T_b = seq_lens[b] (clamped to [0, cap]): its bitmap words
+//     at that row, its kept values in ascending channel order right after the
+//     values already stored for (b, h), i.e. from the tile-offset end entry
+//     tile_off[ceil(T_b / 64)] (0 for an empty sequence, whose entry 0 is
+//     written as 0);
+//   - the end entry of the grown sequence, tile_off[ceil((T_b + 1) / 64)], is
+//     set to that start plus keep.
+// A sequence already at capacity is left unchanged and bit 0 of *status is
+// set.  seq_lens is not changed here: the key and value tensors of a step
+// share one length, which the caller advances once after appending to both.
+int orc_append_rows(uint64_t* bitmaps, uint16_t* values, uint32_t* tile_off, int B, int H,
+                    int64_t cap, int d, int k, const int32_t* head_keep, const uint16_t* rows,
+                    const int32_t* seq_lens, uint32_t* status) {
+  if (d <= 0 || d % 64 != 0 || cap <= 0 || cap % 64 != 0 || k < 0 || k > d) return -1;
+  Layout L;
+  if (!make_layout(H, head_keep, k, d, cap, &L)) return -1;
+  const int words = d / 64;
+  const int64_t ntile_entries = cap / 64 + 1;
+  std::vector<uint8_t> keep(d);
+  for (int64_t u = 0; u < static_cast<int64_t>(B) * H; ++u) {
+    const int64_t b = u / H, h = u % H;
+    const int T = clamp_len(seq_lens[b], cap);
+    if (T >= cap) {
+      if (status) *status |= 1u;
+      continue;
+    }
+    const uint16_t* x = rows + u * d;
+    uint64_t* bm = bitmaps + (u * cap + T) * words;
+    uint16_t* val = values + L.region(b, h);
+    uint32_t* toff = tile_off + u * ntile_entries;
+    if (T == 0) toff[0] = 0;
+    const uint32_t start = toff[(T + 63) / 64];
+    prune_row(x, d, static_cast<int>(L.keep[h]), keep.data());
+    for (int w = 0; w < words; ++w) bm[w] = 0;
+    uint32_t n = 0;
+    for (int c = 0; c < d; ++c) {
+      if (keep[c]) {
+        bm[c / 64] |= uint64_t{1} << (c % 64);
+        val[start + n++] = x[c];
+      }
+    }
+    toff[(T + 1 + 63) / 64] = start + n;
+  }
+  return 0;
+}
+
 // Decompress (R7): walk the bitmap; a set bit takes the next stored value, a
 // clear bit gives +0.0.  Output [B][H][cap][d] fp16 bits; rows >= T_b are zero.
 int orc_decompress_hk(const uint64_t* bitmaps, const uint16_t* values, const uint32_t* tile_off,
