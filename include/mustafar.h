@@ -55,6 +55,9 @@ typedef enum {
 
 /* Sticky device status bits written by mustafar_append_token. */
 #define MUSTAFAR_STATUS_APPEND_FULL 1u /* a sequence was already at capacity; its row was dropped */
+#define MUSTAFAR_STATUS_BAD_OFFSETS 2u /* a tile-offset end entry would have placed a new row's values
+                                          outside its (batch, head) value region; that row (bitmap,
+                                          values, offsets) was not written */
 
 /*
  * One compressed tensor (the key cache or the value cache of one layer) in the
@@ -172,6 +175,16 @@ int mustafar_prune_compress(const mustafar_kv_t *dst, const uint16_t *dense, int
  *   status       (device) uint32, may be NULL; MUSTAFAR_STATUS_APPEND_FULL is
  *                OR-ed in when a sequence is already at capacity (that
  *                sequence is then left unchanged).
+ *
+ * Offsets precondition: for T_b > 0 the new row's values are placed at the
+ * tile-offset end entry tile_offsets[ceil(T_b / 64)], which every call of this
+ * library leaves consistent with the stored rows (prefill, append, fused
+ * step).  For T_b = 0 the entries are not read: the row starts at value 0 and
+ * entry 0 is written, so a never-prefilled cache (any contents) can be grown
+ * from empty.  An end entry that would put the row's values past the
+ * (batch, head) value region (capacity * keep values) is never followed: that
+ * row is not written, MUSTAFAR_STATUS_BAD_OFFSETS is OR-ed into *status, and
+ * the length still advances (the cache is inconsistent and must be refilled).
  */
 int mustafar_append_token(const mustafar_kv_t *k, const mustafar_kv_t *v, const uint16_t *k_new,
                           const uint16_t *v_new, int32_t *seq_lens, uint32_t *status,
@@ -269,6 +282,8 @@ int mustafar_decode_attn_valu(const uint16_t *q, int32_t num_q_heads, const must
  *                seq_lens[b] + 1 rows, and seq_lens[b] is incremented once.  A
  *                sequence already at capacity adds nothing, attends over its
  *                capacity rows and ORs MUSTAFAR_STATUS_APPEND_FULL into *status.
+ *                The offsets precondition and MUSTAFAR_STATUS_BAD_OFFSETS are
+ *                those of mustafar_append_token.
  *   status       (device) uint32, may be NULL.
  *   max_seq_len  host upper bound of the lengths after the step (picks splits).
  *   Other arguments and errors as mustafar_decode_attn; the caches are written.

@@ -20,6 +20,7 @@ MUSTAFAR_ENODEV = -3
 MUSTAFAR_ELAUNCH = -4
 MUSTAFAR_ENOSPACE = -5
 STATUS_APPEND_FULL = 1
+STATUS_BAD_OFFSETS = 2
 HEAD_DIM = 128
 MAX_HEAD_KEEP = 128
 

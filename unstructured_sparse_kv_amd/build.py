@@ -9,8 +9,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmustafar.so")
-SOURCES = ["api.hip", "prune.hip", "decode_sparse_mfma.hip", "decode_sparse.hip", "decode_24.hip",
-           "decode_dense.hip", "util.hip"]
+# the slowest translation units first, so that the parallel build finishes early
+SOURCES = ["decode_sparse_mfma_g4.hip", "decode_sparse_mfma_g8.hip", "decode_sparse_mfma_g2.hip",
+           "decode_sparse_mfma_g1.hip", "decode_24.hip", "decode_sparse.hip", "decode_dense.hip",
+           "decode_sparse_mfma.hip", "api.hip", "prune.hip", "util.hip"]
 ARCH = os.environ.get("MUSTAFAR_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -22,7 +24,7 @@ FLAGS = [
 # Matrix-core kernels: MFMA accumulators in ordinary VGPRs, so the vector code
 # that rescales them needs no copies to and from the accumulation registers.
 FILE_FLAGS = {
-    "decode_sparse_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    **{f"decode_sparse_mfma_g{g}.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"] for g in (1, 2, 4, 8)},
     "decode_24.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "decode_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }

@@ -158,6 +158,7 @@ int sparse_decode(SparseLauncher launch, const uint16_t* q, int32_t num_q_heads,
   a.part = (float*)workspace;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.status = status;
   hipStream_t st = (hipStream_t)stream;
   if ((rc = launched(launch(a, k->batch, st)))) return rc;
   return launched(launch_decode_reduce(a.part, k->batch, num_q_heads, k->num_kv_heads, sp, out, st,

@@ -75,6 +75,7 @@ struct SparseDecodeArgs {
   // which then covers that row too (matrix-core kernel only)
   const uint16_t* k_new;
   const uint16_t* v_new;
+  uint32_t* status;  // fused step: MUSTAFAR_STATUS_BAD_OFFSETS (may be null)
 };
 
 struct PruneArgs {

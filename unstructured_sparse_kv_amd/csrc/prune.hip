@@ -93,9 +93,15 @@ __global__ __launch_bounds__(1024) void append_kernel(AppendArgs a) {
       const uint32_t x0 = src[lane], x1 = src[lane + 64];
       const RowMask m = select_row(x0, x1, keep);
       // the new row's values go right after the stored ones: the current end
-      // entry of the tile offsets (T * keep when every row holds keep values)
+      // entry of the tile offsets (T * keep when every row holds keep values);
+      // an empty sequence starts at 0 whatever the offsets hold
       uint32_t* toff = (is_v ? a.vtoff : a.ktoff) + unit * ntoff;
-      const uint32_t pos = toff[(T + kTile - 1) / kTile];
+      const uint32_t pos = T == 0 ? 0u : wave_uniform(toff[(T + kTile - 1) / kTile]);
+      if (!append_fits(pos, keep, cap)) {
+        if (lane == 0 && a.status) atomicOr(a.status, MUSTAFAR_STATUS_BAD_OFFSETS);
+        continue;
+      }
+      if (T == 0 && lane == 0) toff[0] = 0;
       uint64_t* bm = (is_v ? a.vbm : a.kbm) + (unit * cap + T) * 2;
       uint16_t* vals = (is_v ? a.vval : a.kval) + region_of(map, at, b, h, cap) + pos;
       store_row(m, x0, x1, bm, vals);

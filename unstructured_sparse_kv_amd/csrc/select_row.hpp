@@ -70,6 +70,14 @@ __device__ __forceinline__ RowMask select_row_24(uint32_t x0, uint32_t x1) {
   return RowMask{__ballot(keep_24(x0 & 0x7FFFu)), __ballot(keep_24(x1 & 0x7FFFu))};
 }
 
+// A new row of `keep` values starting at value `pos` of its (batch, head)
+// value region (capacity * keep values) stays inside the region.  The start
+// comes from the tile-offset end entry in device memory, so it is checked
+// before any store follows it.
+__device__ __forceinline__ bool append_fits(uint32_t pos, int keep, int cap) {
+  return (uint64_t)pos + (uint64_t)keep <= (uint64_t)cap * (uint64_t)keep;
+}
+
 // Writes the row's bitmap words and packs its kept values (ascending channel)
 // at `vals`.
 __device__ __forceinline__ void store_row(const RowMask& m, uint32_t x0, uint32_t x1,
