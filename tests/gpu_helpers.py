@@ -3,6 +3,7 @@ copy results back, compare with the CPU oracle on the same bits."""
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 import torch
@@ -13,6 +14,8 @@ import unstructured_sparse_kv_amd as usk
 MAX_ABS = 1e-2
 MAX_REL_L2 = 1e-3
 SCALE = 1.0 / math.sqrt(128)
+# oracle threads: the CPU share a GPU test may use (16 per GPU), whatever the host shows
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def say(msg: str) -> None:

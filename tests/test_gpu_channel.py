@@ -41,14 +41,16 @@ def _run(fn, q, kc, vc, seq_d, max_len, splits=0):
     return out.float().cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("kk,kv", [(38, 38), (64, 64), (2, 126), (0, 128), (38, 8)])
-def test_channel_wise_compress_and_decode(gpu, kk, kv):
-    B, Hq, Hkv, T, cap = 3, 8, 2, 300, 320
+@pytest.mark.parametrize("kk,kv,G", [(38, 38, 4), (64, 64, 4), (2, 126, 4), (0, 128, 4), (38, 8, 4),
+                                     (38, 38, 8), (64, 64, 8)])
+def test_channel_wise_compress_and_decode(gpu, kk, kv, G):
+    B, Hkv, T, cap = 3, 2, 300, 320
+    Hq = G * Hkv
     K, V, q = _inputs(B, Hq, Hkv, T, 500 + kk * 7 + kv)
     K[0, 0, :64, 5] = 0.25          # a column of equal keys: ties to the earlier rows
     K[1, 1, 70, :] = 60.0           # a row that wins every channel of its tile
     seq = np.array([300, 256, 37], np.int32)
-    say(f"channel-wise keep K={kk} V={kv}")
+    say(f"channel-wise keep K={kk} V={kv} G={G}")
     seq_d = torch.from_numpy(seq).to(gpu)
     kc, vc = _compress(K.to(gpu), seq_d, kk, cap), _compress(V.to(gpu), seq_d, kv, cap)
     torch.cuda.synchronize()
@@ -100,27 +102,14 @@ def test_channel_wise_then_decode_steps(gpu):
             for x, y in zip(c1.views(), c2.views()):
                 assert torch.equal(x, y), f"step {step}: caches differ"
     assert st.item() == 0
-    # oracle: channel-wise prefill, then the appended rows pruned per token
-    seq = seq0 + 3
+    # oracle: channel-wise prefill, then the oracle's append (new rows pruned per token)
     ko = oracle.compress_channel(K, seq0, keep, cap)
     vo = oracle.compress_channel(V, seq0, keep, cap)
-    for b in range(B):
-        for i, (kn, vn) in enumerate(news):
-            r = int(seq0[b]) + i
-            for c, new in ((ko, kn), (vo, vn)):
-                for h in range(Hkv):
-                    row = new[b, h].numpy().view(np.uint16)
-                    mask = oracle.prune_rows(row[None], keep)[0]
-                    words = [0, 0]
-                    for ch in range(128):
-                        if mask[ch]:
-                            words[ch // 64] |= 1 << (ch % 64)
-                    c.bitmaps[b, h, r] = np.array(words, dtype=np.uint64)
-                    pos = int(c.tile_off[b, h, r // 64]) + sum(
-                        bin(int(w)).count("1") for rr in range(64 * (r // 64), r)
-                        for w in c.bitmaps[b, h, rr])
-                    c.values[b, h, pos:pos + keep] = row[mask == 1]
-                    c.tile_off[b, h, (r + 1 + 63) // 64] = pos + keep
+    seq = seq0.copy()
+    for kn, vn in news:
+        seq, st_o = oracle.append_step(ko, vo, kn, vn, seq)
+        assert st_o == 0
+    assert np.array_equal(seq, seq0 + 3)
     assert_compressed_equal(kb, ko, seq)
     assert_compressed_equal(vb, vo, seq)
     ref = oracle.attention_compressed(qs.cpu(), ko, vo, seq, SCALE)

@@ -60,6 +60,7 @@ def _decode(fn, q, kc, vc, seq_d, max_len, splits=0):
     ([26, 50, 0, 128, 38, 37], [37, 38, 128, 0, 50, 26], 2),   # every bucket edge, keep 0 and 128
     ([28, 32, 34, 38, 38, 42, 44, 48], [48, 44, 42, 38, 38, 34, 32, 28], 4),  # mean 38
     ([38, 38, 64, 64], [64, 64, 38, 38], 1),
+    ([28, 32, 34, 38, 38, 42, 44, 48], [48, 44, 42, 38, 38, 34, 32, 28], 8),  # 64 q / 8 kv heads
 ])
 def test_head_keep_compress_and_decode(gpu, kheads, vheads, G):
     Hkv = len(kheads)
@@ -84,16 +85,17 @@ def test_head_keep_compress_and_decode(gpu, kheads, vheads, G):
             assert_attn_close(got, ref, f"per-head {variant} splits={splits}")
 
 
-def test_head_keep_decode_step(gpu):
+@pytest.mark.parametrize("G", [4, 8])
+def test_head_keep_decode_step(gpu, G):
     """Fused steps over per-head caches: bit for bit the same as append + decode,
     and the final caches and attention match the oracle on the grown caches."""
     kheads, vheads = [28, 32, 34, 38, 38, 42, 44, 48], [48, 44, 42, 38, 38, 34, 32, 28]
-    Hkv, G = len(kheads), 4
+    Hkv = len(kheads)
     B, T, cap = 3, 190, 256
     Hq = G * Hkv
     K, V, q = _inputs(B, Hq, Hkv, cap, 99)
     seq0 = np.array([190, 64, 0], np.int32)
-    say("per-head keep: fused steps vs separate calls")
+    say(f"per-head keep: fused steps vs separate calls G={G}")
     seq_a = torch.from_numpy(seq0).to(gpu)
     seq_b = seq_a.clone()
     ka, va = _compress(K.to(gpu), seq_a, kheads, cap), _compress(V.to(gpu), seq_a, vheads, cap)

@@ -11,8 +11,8 @@ import torch
 import oracle
 import synth
 import unstructured_sparse_kv_amd as usk
-from tests.gpu_helpers import (SCALE, assert_attn_close, assert_compressed_equal, compress_on_gpu,
-                               oracle_attention_units, say, u16)
+from tests.gpu_helpers import (ORACLE_THREADS, SCALE, assert_attn_close, assert_compressed_equal,
+                               compress_on_gpu, oracle_attention_units, say, u16)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -175,7 +175,13 @@ def test_llama2_layer_full(gpu):
     assert_attn_close(_f64(outd), oracle.attention_dense(q, K, V, seq, SCALE), "llama2 dense")
 
 
-def test_llama3_layer_sampled(gpu):
+def test_llama3_layer_full(gpu):
+    """The Llama-3-8B-shaped layer at full size (B=8, 32/8 heads, T=32768, keep 38):
+    every (batch, kv head) unit's key and value caches bit for bit against the
+    oracle's compression of the same dense bits, every one of the 256 outputs of
+    both sparse kernels at splits 0, 1, 7 and 64 within tolerance of the oracle's
+    attention over its own caches, determinism, and the dense baseline's 256
+    outputs against the oracle's dense attention."""
     cfg = synth.CONFIGS["llama3_8b_layer"]
     say("llama3 layer: generating B=8 Hkv=8 T=32768 on the GPU")
     K, V, q, seq = synth.make_inputs(cfg, device=gpu)
@@ -184,37 +190,72 @@ def test_llama3_layer_sampled(gpu):
     kc = compress_on_gpu(K, seq_d, keep, cfg.T)
     vc = compress_on_gpu(V, seq_d, keep, cfg.T)
     torch.cuda.synchronize()
-    units = [(0, 0), (3, 5), (7, 7)]
-    Kc = torch.stack([K[b, h] for b, h in units])[:, None].cpu()
-    Vc = torch.stack([V[b, h] for b, h in units])[:, None].cpu()
-    seq_u = np.array([cfg.T] * len(units), np.int32)
-    ko, vo = oracle.compress(Kc, seq_u, keep, cfg.T), oracle.compress(Vc, seq_u, keep, cfg.T)
-    say("llama3 layer: bit-exact check of sampled units")
-    assert_compressed_equal(kc, ko, seq.numpy(), units, [(i, 0) for i in range(len(units))])
-    assert_compressed_equal(vc, vo, seq.numpy(), units, [(i, 0) for i in range(len(units))])
-    pairs = [(0, 0), (0, 3), (3, 21), (7, 31)]
     Kcpu, Vcpu, qcpu = K.cpu(), V.cpu(), q.cpu()
-    ref = oracle_attention_units(qcpu, Kcpu, Vcpu, seq.numpy(), keep, keep, cfg.T, pairs, 4)
-    refd = {}
-    for b, hq in pairs:
-        h = hq // 4
-        refd[(b, hq)] = oracle.attention_dense(qcpu[b:b + 1, hq:hq + 1], Kcpu[b:b + 1, h:h + 1],
-                                               Vcpu[b:b + 1, h:h + 1], [cfg.T], SCALE)[0, 0]
+    say(f"llama3 layer: oracle compression of all 64 units ({ORACLE_THREADS} threads)")
+    ko = oracle.compress(Kcpu, seq, keep, cfg.T, nthreads=ORACLE_THREADS)
+    vo = oracle.compress(Vcpu, seq, keep, cfg.T, nthreads=ORACLE_THREADS)
+    say("llama3 layer: bit-exact check of all units")
+    assert_compressed_equal(kc, ko, seq.numpy())
+    assert_compressed_equal(vc, vo, seq.numpy())
+    assert kc.used_bytes(seq.numpy()) + vc.used_bytes(seq.numpy()) == 2 * 193069312
+    say("llama3 layer: oracle attention, all 256 (batch, q head) pairs")
+    ref = oracle.attention_compressed(qcpu, ko, vo, seq, SCALE, nthreads=ORACLE_THREADS)
     for variant in SPARSE:
         outs = {}
         for splits in (0, 1, 7, 64):
             say(f"llama3 layer: sparse decode ({variant}) splits={splits}")
             out = _decode(q, kc, vc, seq_d, cfg.T, splits, variant)
             outs[splits] = out.clone()
-            got = np.stack([_f64(out[b, hq]) for b, hq in pairs])
-            assert_attn_close(got, np.stack([ref[p] for p in pairs]),
-                              f"llama3 sparse {variant} splits={splits}")
+            assert_attn_close(_f64(out), ref, f"llama3 sparse {variant} splits={splits}")
         again = _decode(q, kc, vc, seq_d, cfg.T, 0, variant)
         assert torch.equal(again, outs[0]), f"decode ({variant}) is not deterministic"
-    say("llama3 layer: dense baseline")
+    say("llama3 layer: dense baseline, all 256 pairs")
+    refd = oracle.attention_dense(qcpu, Kcpu, Vcpu, seq, SCALE, nthreads=ORACLE_THREADS)
     outd = _dense(q, K, V, seq_d, cfg.T)
-    got = np.stack([_f64(outd[b, hq]) for b, hq in pairs])
-    assert_attn_close(got, np.stack([refd[p] for p in pairs]), "llama3 dense")
+    assert_attn_close(_f64(outd), refd, "llama3 dense")
+
+
+@pytest.mark.parametrize("B,T,Hq,layer", [(32, 131072, 32, 0), (64, 16384, 32, 31), (1, 16384, 64, 5)])
+def test_llama3_stack_points(gpu, B, T, Hq, layer):
+    """Points of the 32-layer stack sweep, one layer each, at their full shape
+    (the largest batch x length the sweep times, the largest batch, and a 64 q /
+    8 kv head group of 8): the layer is generated, pruned, compressed and
+    attended on the GPU; sampled units -- the first, a middle one and the last --
+    bit for bit, and sampled (batch, q head) outputs of both sparse kernels
+    within tolerance of the oracle."""
+    cfg = synth.CONFIGS["llama3_8b_stack"]
+    keep = usk.keep_from_sparsity(cfg.sparsity)
+    Hkv = cfg.Hkv
+    G = Hq // Hkv
+    say(f"stack point B={B} T={T} Hq={Hq} layer={layer}: generating on the GPU")
+    K, V, q, _ = synth.make_inputs(cfg, device=gpu, layer=layer, B=B, T=T)
+    if Hq != cfg.Hq:
+        q = synth.normal_f16(cfg.seed, synth.S_Q, layer, (B, Hq, 128), gpu)
+    seq_d = torch.full((B,), T, dtype=torch.int32, device=gpu)
+    kc = compress_on_gpu(K, seq_d, keep, T)
+    vc = compress_on_gpu(V, seq_d, keep, T)
+    outs = {v: _decode(q, kc, vc, seq_d, T, 0, v) for v in SPARSE}
+    seq = np.full(B, T, np.int32)
+    units = sorted({(0, 0), (B // 2, 3), (B - 1, Hkv - 1)})
+    pairs = [(0, 0), (B // 2, 3 * G + 1), (B - 1, Hq - 1)]
+    qcpu = q.cpu()
+    refs = {}
+    for b, h in units:
+        say(f"stack point B={B} T={T}: unit {(b, h)} against the oracle")
+        s1 = np.array([T], np.int32)
+        Kb, Vb = K[b:b + 1, h:h + 1].cpu(), V[b:b + 1, h:h + 1].cpu()
+        ko = oracle.compress(Kb, s1, keep, T, nthreads=ORACLE_THREADS)
+        vo = oracle.compress(Vb, s1, keep, T, nthreads=ORACLE_THREADS)
+        assert_compressed_equal(kc, ko, seq, [(b, h)], [(0, 0)])
+        assert_compressed_equal(vc, vo, seq, [(b, h)], [(0, 0)])
+        for pb, hq in pairs:
+            if pb == b and hq // G == h:
+                refs[(pb, hq)] = oracle.attention_compressed(qcpu[b:b + 1, hq:hq + 1], ko, vo, s1,
+                                                             SCALE)[0, 0]
+    assert set(refs) == set(pairs)
+    for v, out in outs.items():
+        got = np.stack([_f64(out[b, hq]) for b, hq in pairs])
+        assert_attn_close(got, np.stack([refs[p] for p in pairs]), f"stack B={B} T={T} Hq={Hq} {v}")
 
 
 def test_llama3_stack_sampled(gpu):
@@ -252,16 +293,17 @@ def test_llama3_stack_sampled(gpu):
             assert_attn_close(got, np.stack([ref[p] for p in pairs]), f"stack layer {layer} {v}")
 
 
-@pytest.mark.parametrize("keep", [38, 64, 37])
-def test_decode_step_matches_separate_calls(gpu, keep):
+@pytest.mark.parametrize("keep,G", [(38, 4), (64, 4), (37, 4), (38, 8), (64, 8), (13, 8)])
+def test_decode_step_matches_separate_calls(gpu, keep, G):
     """The fused step (mustafar_decode_step) against mustafar_append_token +
     mustafar_decode_attn on copies of the same caches: out, caches, seq_lens
     and status bit for bit, over steps that start a tile, fill an empty
     sequence, and hit capacity."""
-    B, Hq, Hkv, T, cap = 4, 8, 2, 320, 320
-    K, V, q = _small_inputs(B, Hq, Hkv, T, 777 + keep)
+    B, Hkv, T, cap = 4, 2, 320, 320
+    Hq = G * Hkv
+    K, V, q = _small_inputs(B, Hq, Hkv, T, 777 + keep + G)
     seq0 = np.array([130, 64, 0, 318], np.int32)
-    say(f"fused step vs separate calls: keep={keep}")
+    say(f"fused step vs separate calls: keep={keep} G={G}")
     seq_a = torch.from_numpy(seq0).to(gpu)
     seq_b = seq_a.clone()
     ka = compress_on_gpu(K.to(gpu), seq_a, keep, cap)
@@ -296,22 +338,32 @@ def test_decode_step_matches_separate_calls(gpu, keep):
 
 @pytest.mark.parametrize("mode", ["separate", "fused"])
 def test_ragged_append_sequence(gpu, mode):
+    """The Mistral-shaped ragged batch (B=16, 32/8 heads, lengths uniform in
+    [4096, 32768], keep 64) through 64 decode steps, each appending one key and
+    value row per (sequence, kv head) and attending: all 512 outputs at steps 1,
+    2, 32 and 64 within tolerance of the oracle, whose caches grow by its own
+    append; all 128 units' caches bit for bit after step 64; lengths exact."""
     cfg = synth.CONFIGS["mistral_ragged_append"]
     keep = usk.keep_from_sparsity(cfg.sparsity)
     seq0 = synth.seq_lens_uniform(cfg.seed, cfg.B, *cfg.ragged)
     Tmax = cfg.ragged[1]
     cap = Tmax + 64
     say(f"ragged append: B=16 Hkv=8 lens {seq0.min().item()}..{seq0.max().item()} keep={keep} "
-        f"steps={cfg.steps}")
+        f"steps={cfg.steps} mode={mode}")
     K, V, _, _ = synth.make_inputs(cfg, device=gpu, T=cap)
     seq_d = seq0.to(gpu)
     kc = compress_on_gpu(K, seq_d, keep, cap)
     vc = compress_on_gpu(V, seq_d, keep, cap)
+    torch.cuda.synchronize()
+    say(f"ragged append: oracle compression of all 128 units ({ORACLE_THREADS} threads)")
+    seq_o = seq0.numpy().astype(np.int32)
+    ko = oracle.compress(K.cpu(), seq_o, keep, cap, nthreads=ORACLE_THREADS)
+    vo = oracle.compress(V.cpu(), seq_o, keep, cap, nthreads=ORACLE_THREADS)
+    del K, V
     status = torch.zeros(1, dtype=torch.int32, device=gpu)
     ws = usk.make_workspace(cfg.B, cfg.Hq, cfg.Hkv, cap)
     out = torch.empty((cfg.B, cfg.Hq, 128), dtype=torch.float16, device=gpu)
     outv = torch.empty_like(out)
-    pairs = [(0, 0), (5, 13), (9, 30), (15, 7)]
     check_steps = {1, 2, 32, cfg.steps}
     for step in range(1, cfg.steps + 1):
         kn, vn, q = synth.step_inputs(cfg, step - 1, device=gpu)
@@ -321,33 +373,19 @@ def test_ragged_append_sequence(gpu, mode):
             usk.append_token(kc, vc, kn, vn, seq_d, status)
             usk.decode_attn(q, kc, vc, seq_d, cap, SCALE, out, ws)
             usk.decode_attn_valu(q, kc, vc, seq_d, cap, SCALE, outv, ws)
-        # the oracle sees the same new rows written into its dense copy
-        T_old = seq0 + (step - 1)
-        for b in range(cfg.B):
-            K[b, :, T_old[b]] = kn[b]
-            V[b, :, T_old[b]] = vn[b]
+        seq_o, st = oracle.append_step(ko, vo, kn.cpu(), vn.cpu(), seq_o)
+        assert st == 0
         if step in check_steps:
             torch.cuda.synchronize()
-            seq_now = (seq0 + step).numpy()
-            assert np.array_equal(seq_d.cpu().numpy(), seq_now)
-            say(f"ragged append: step {step} parity")
-            qcpu = q.cpu()
-            got, gotv, exp = [], [], []
-            for b, hq in pairs:
-                h = hq // 4
-                T = int(seq_now[b])
-                s1 = np.array([T], np.int32)
-                ko = oracle.compress(K[b:b + 1, h:h + 1, :T].cpu(), s1, keep, cap)
-                vo = oracle.compress(V[b:b + 1, h:h + 1, :T].cpu(), s1, keep, cap)
-                exp.append(oracle.attention_compressed(qcpu[b:b + 1, hq:hq + 1], ko, vo, s1, SCALE)[0, 0])
-                got.append(_f64(out[b, hq]))
-                gotv.append(_f64(outv[b, hq]))
-                if step == cfg.steps:
-                    assert_compressed_equal(kc, ko, seq_now, [(b, h)], [(0, 0)])
-                    assert_compressed_equal(vc, vo, seq_now, [(b, h)], [(0, 0)])
-            assert_attn_close(np.stack(got), np.stack(exp), f"ragged append step {step}")
+            assert np.array_equal(seq_d.cpu().numpy(), seq_o)
+            say(f"ragged append: step {step} parity, all 512 outputs")
+            ref = oracle.attention_compressed(q.cpu(), ko, vo, seq_o, SCALE, nthreads=ORACLE_THREADS)
+            assert_attn_close(_f64(out), ref, f"ragged append step {step} ({mode})")
             if mode == "separate":
-                assert_attn_close(np.stack(gotv), np.stack(exp), f"ragged append step {step} valu")
+                assert_attn_close(_f64(outv), ref, f"ragged append step {step} valu")
+    say("ragged append: all 128 units bit for bit after the last step")
+    assert_compressed_equal(kc, ko, seq_o)
+    assert_compressed_equal(vc, vo, seq_o)
     assert status.item() == 0
 
 
