@@ -39,9 +39,14 @@ def build(extra_flags: tuple = ()) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        # MUSTAFAR_ORACLE_LIB names another build of the same source (the CPU
+        # sanitizer test loads an ASan/UBSan build this way)
+        path = os.environ.get("MUSTAFAR_ORACLE_LIB")
+        if path is None:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        L = ctypes.CDLL(path)
         L.orc_half_to_double.restype = F64
         L.orc_half_to_double.argtypes = [ctypes.c_uint16]
         L.orc_half_to_double_array.argtypes = [P, I64, P]
