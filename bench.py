@@ -50,7 +50,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "sparse decode-attn GB/s (% HBM peak) + speedup vs dense fp16, Llama-3-8B shape 70%"
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the timed decode call (split kernel, its helpers, the merge kernel, the launcher)
-DECODE_SOURCES = ["decode_sparse_mfma.hip", "decode_walk.hpp", "merge.hpp", "tile_softmax.hpp", "device_common.hpp",
+DECODE_SOURCES = ["decode_sparse_mfma.hpp", "decode_sparse_mfma_g4.hip", "decode_walk.hpp", "merge.hpp", "tile_softmax.hpp", "device_common.hpp",
                   "kernels.hpp", "select_row.hpp", "util.hip", "api.hip"]
 DECODE_KERNELS = "decode_sparse_mfma_kernel<4,40,38> + decode_reduce_kernel"
 
@@ -187,6 +187,283 @@ def stack_sweep(args) -> int:
     return 0
 
 
+def _timed(stream, fn, n, before=None):
+    """n calls of fn, each bracketed by its own pair of HIP events on `stream`
+    (after `before`, which is not timed); returns the seconds of each."""
+    import torch
+    ts = []
+    for _ in range(n):
+        if before is not None:
+            before()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    return ts
+
+
+def _oracle_threads():
+    import oracle
+    hw = oracle.hardware_threads()
+    nproc = len(os.sched_getaffinity(0))
+    # the GPU box grants each GPU a 16-core share of the host, whatever the host shows
+    return hw, nproc, max(1, min(16, nproc))
+
+
+def _caches_equal(c, o, seq, keep):
+    import numpy as np
+    bm, vals, toff = (t.cpu().numpy() for t in c.views())
+    bm, vals, toff = bm.view(np.uint64), vals.view(np.uint16), toff.view(np.uint32)
+    for b in range(c.batch):
+        T = int(seq[b])
+        nt = (T + 63) // 64 + 1
+        if not (np.array_equal(bm[b, :, :T], o.bitmaps[b, :, :T])
+                and np.array_equal(vals[b, :, :T * keep], o.values[b, :, :T * keep])
+                and np.array_equal(toff[b, :, :nt], o.tile_off[b, :, :nt])):
+            return False
+    return True
+
+
+def bench_llama2_layer(args) -> int:
+    """The Llama-2-7B-shaped layer at batch 1 (32/32 heads, T=4096, keep 38): its
+    compressed caches (24 MB) fit in the 256 MB last-level cache, so every timed
+    step follows a 1 GiB read of other memory.  A step is one fused
+    mustafar_decode_step (append one row per kv head, attend)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import unstructured_sparse_kv_amd as usk
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    cfg = synth.CONFIGS["llama2_7b_layer"]
+    B, Hq, Hkv, T0, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.T, cfg.d
+    keep = usk.keep_from_sparsity(cfg.sparsity)
+    scale = 1.0 / math.sqrt(d)
+    total = args.warmup + args.steps
+    cap = (T0 + total + 63) // 64 * 64
+    K, V, _, _ = synth.make_inputs(cfg, device=dev, T=cap)
+    seq_d = torch.full((B,), T0, dtype=torch.int32, device=dev)
+    kc, vc = usk.CompressedKV(B, Hkv, keep, cap, dev), usk.CompressedKV(B, Hkv, keep, cap, dev)
+    pre = _timed(stream, lambda: (usk.prune_compress(kc, K, seq_d), usk.prune_compress(vc, V, seq_d)), 3)
+    steps_in = [synth.step_inputs(cfg, i, device=dev) for i in range(total)]
+    ws = usk.make_workspace(B, Hq, Hkv, cap)
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    before = lambda: usk.probe_stream_read(flush, sink)  # noqa: E731
+    # clock ramp: read-only decode calls
+    t_r = time.perf_counter()
+    while time.perf_counter() - t_r < args.ramp_s:
+        for _ in range(50):
+            usk.decode_attn(steps_in[0][2], kc, vc, seq_d, cap, scale, out, ws)
+        torch.cuda.synchronize()
+    it = iter(range(total))
+    step_fn = lambda: (lambda i: usk.decode_step(steps_in[i][2], kc, vc, steps_in[i][0], steps_in[i][1],  # noqa: E731
+                                                 seq_d, cap, scale, out, ws, status))(next(it))
+    _timed(stream, step_fn, args.warmup, before)
+    ts = _timed(stream, step_fn, args.steps, before)
+    assert status.item() == 0
+    L = T0 + total
+    seq_fin = np.full(B, L, np.int32)
+    step_s = median(ts)
+    nbytes = kc.used_bytes(np.full(B, L - 1, np.int32)) + vc.used_bytes(np.full(B, L - 1, np.int32))
+    achieved = nbytes / step_s / 1e9
+    # read-only decode at the final length, after the same read, and the dense kernel
+    dec_s = median(_timed(stream, lambda: usk.decode_attn(steps_in[-1][2], kc, vc, seq_d, cap, scale,
+                                                          out, ws), 20, before))
+    wsd = usk.make_workspace(B, Hq, Hkv, T0)
+    outd = torch.empty_like(out)
+    seq_t0 = torch.full((B,), T0, dtype=torch.int32, device=dev)
+    dense_s = median(_timed(stream, lambda: usk.dense_decode_attn(steps_in[-1][2], K, V, seq_t0, T0, scale,
+                                                                  outd, wsd), 20, before))
+    comp_t0 = kc.used_bytes(np.full(B, T0, np.int32)) + vc.used_bytes(np.full(B, T0, np.int32))
+    dense_bytes = 2 * B * Hkv * T0 * d * 2
+    log(f"llama2 layer: fused step {step_s * 1e6:.2f} us ({achieved:.0f} GB/s, "
+        f"{achieved / HBM_PEAK_GBS:.1%}); decode only {dec_s * 1e6:.2f} us; dense {dense_s * 1e6:.2f} us")
+    # oracle: same prefill bits, its own appends, the last step's query
+    usk.decode_attn(steps_in[-1][2], kc, vc, seq_d, cap, scale, out, ws)
+    torch.cuda.synchronize()
+    hw, nproc, nth = _oracle_threads()
+    Kc, Vc = K[:, :, :T0].cpu(), V[:, :, :T0].cpu()
+    seq0 = np.full(B, T0, np.int32)
+    c0 = time.perf_counter()
+    ko = oracle.compress(Kc, seq0, keep, cap, nthreads=nth)
+    vo = oracle.compress(Vc, seq0, keep, cap, nthreads=nth)
+    cpu_pre = time.perf_counter() - c0
+    seq_o = seq0
+    for i in range(total):
+        seq_o, st = oracle.append_step(ko, vo, steps_in[i][0].cpu(), steps_in[i][1].cpu(), seq_o)
+    c0 = time.perf_counter()
+    ref = oracle.attention_compressed(steps_in[-1][2].cpu(), ko, vo, seq_o, scale, nthreads=nth)
+    cpu_s = time.perf_counter() - c0
+    got = out.float().cpu().numpy().astype(np.float64)
+    exact = _caches_equal(kc, ko, seq_fin, keep) and _caches_equal(vc, vo, seq_fin, keep)
+    err = float(np.abs(got - ref).max())
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    ok = exact and err <= 1e-2 and rel <= 1e-3
+    res = {
+        "metric": "sparse decode step GB/s (% HBM peak), Llama-2-7B layer at batch 1, after a 1 GiB read",
+        "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16 in, f32 accumulate", "data": "synthetic (seeded)",
+        "config": {"workload": "llama2_7b_layer: B=1, 32 q / 32 kv heads, head_dim 128, T=4096, keep 38; "
+                               "step = mustafar_decode_step after a 1 GiB read of other memory",
+                   "batch": B, "q_heads": Hq, "kv_heads": Hkv, "seq_len": T0, "keep": keep},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(nbytes), "avg_launch_us": round(step_s * 1e6, 2)},
+        "cpu_baseline": {"value": round(nbytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+                         "hardware_concurrency": hw, "nproc": nproc, "prefill_compress_s": round(cpu_pre, 4),
+                         "sample": "the whole workload: prefill prune + compress of K and V and one decode "
+                                   f"step over all {B * Hq} (batch, q head) pairs"},
+        "extra": {"decode_only_us": round(dec_s * 1e6, 2), "dense_us": round(dense_s * 1e6, 2),
+                  "speedup_vs_dense": round(dense_s / dec_s, 3),
+                  "prefill_compress_us": round(median(pre) * 1e6, 2),
+                  "compressed_kv_bytes": int(comp_t0), "dense_kv_bytes": int(dense_bytes),
+                  "step_us_all": [round(t * 1e6, 2) for t in ts],
+                  "parity": {"caches_bit_exact": bool(exact), "max_abs": err, "rel_l2": rel}},
+    }
+    print(json.dumps(res), flush=True)
+    return 0 if ok else 3
+
+
+def bench_ragged_append(args) -> int:
+    """The Mistral-shaped ragged batch (B=16, 32 q / 8 kv heads, lengths uniform in
+    [4096, 32768], keep 64): 64 fused decode steps, each appending one key and
+    value row per (sequence, kv head) and attending.  Timed back to back with one
+    event pair (the whole sequence), then per step in a second pass of 64 steps."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import unstructured_sparse_kv_amd as usk
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    cfg = synth.CONFIGS["mistral_ragged_append"]
+    B, Hq, Hkv, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.d
+    keep = usk.keep_from_sparsity(cfg.sparsity)
+    scale = 1.0 / math.sqrt(d)
+    nsteps = cfg.steps
+    seq0 = synth.seq_lens_uniform(cfg.seed, B, *cfg.ragged).numpy().astype(np.int32)
+    Tmax = cfg.ragged[1]
+    cap = (Tmax + 2 * nsteps + 63) // 64 * 64
+    K, V, _, _ = synth.make_inputs(cfg, device=dev, T=cap)
+    seq_d = torch.from_numpy(seq0).to(dev)
+    kc, vc = usk.CompressedKV(B, Hkv, keep, cap, dev), usk.CompressedKV(B, Hkv, keep, cap, dev)
+    usk.prune_compress(kc, K, seq_d)
+    usk.prune_compress(vc, V, seq_d)
+    steps_in = [synth.step_inputs(cfg, i, device=dev) for i in range(2 * nsteps)]
+    ws = usk.make_workspace(B, Hq, Hkv, cap)
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    t_r = time.perf_counter()
+    while time.perf_counter() - t_r < args.ramp_s:
+        for _ in range(20):
+            usk.decode_attn(steps_in[0][2], kc, vc, seq_d, cap, scale, out, ws)
+        torch.cuda.synchronize()
+
+    def step(i):
+        kn, vn, q = steps_in[i]
+        usk.decode_step(q, kc, vc, kn, vn, seq_d, cap, scale, out, ws, status)
+
+    def step_bytes(i):  # compressed bytes the step reads (lengths after its append)
+        sh = np.minimum(seq0 + i + 1, cap)
+        return kc.used_bytes(sh) + vc.used_bytes(sh)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(nsteps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    seq_total = e0.elapsed_time(e1) * 1e-3
+    total_bytes = sum(step_bytes(i) for i in range(nsteps))
+    per = []
+    for i in range(nsteps, 2 * nsteps):
+        per.append(_timed(stream, lambda: step(i), 1)[0])
+    assert status.item() == 0
+    per_gbs = [step_bytes(nsteps + j) / t / 1e9 for j, t in enumerate(per)]
+    value = total_bytes / seq_total / 1e9
+    log(f"ragged append: 64 fused steps in {seq_total * 1e3:.3f} ms ({value:.0f} GB/s, "
+        f"{value / HBM_PEAK_GBS:.1%}); per step {median(per) * 1e6:.1f} us median")
+    # dense comparison over the final lengths (the dense caches of the prefill rows)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    seq_pre = torch.from_numpy(seq0).to(dev)
+    wsd = usk.make_workspace(B, Hq, Hkv, cap)
+    outd = torch.empty_like(out)
+    dense_s = median(_timed(stream, lambda: usk.dense_decode_attn(steps_in[-1][2], K, V, seq_pre, Tmax, scale,
+                                                                  outd, wsd), 10,
+                            lambda: usk.probe_stream_read(flush, sink)))
+    sparse_s = median(_timed(stream, lambda: usk.decode_attn(steps_in[-1][2], kc, vc, seq_pre, Tmax, scale,
+                                                             outd, ws), 10,
+                             lambda: usk.probe_stream_read(flush, sink)))
+    del flush
+    # oracle: prefill from the same dense bits, its own 128 appends, the last query
+    usk.decode_attn(steps_in[-1][2], kc, vc, seq_d, cap, scale, out, ws)
+    torch.cuda.synchronize()
+    hw, nproc, nth = _oracle_threads()
+    c0 = time.perf_counter()
+    ko = oracle.compress(K.cpu(), seq0, keep, cap, nthreads=nth)
+    vo = oracle.compress(V.cpu(), seq0, keep, cap, nthreads=nth)
+    cpu_pre = time.perf_counter() - c0
+    seq_o = seq0
+    c0 = time.perf_counter()
+    for i in range(2 * nsteps):
+        seq_o, st = oracle.append_step(ko, vo, steps_in[i][0].cpu(), steps_in[i][1].cpu(), seq_o)
+    cpu_app = time.perf_counter() - c0
+    c0 = time.perf_counter()
+    ref = oracle.attention_compressed(steps_in[-1][2].cpu(), ko, vo, seq_o, scale, nthreads=nth)
+    cpu_s = time.perf_counter() - c0
+    got = out.float().cpu().numpy().astype(np.float64)
+    exact = _caches_equal(kc, ko, seq_o, keep) and _caches_equal(vc, vo, seq_o, keep)
+    err = float(np.abs(got - ref).max())
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    ok = exact and err <= 1e-2 and rel <= 1e-3 and np.array_equal(seq_d.cpu().numpy(), seq_o)
+    last_bytes = step_bytes(2 * nsteps - 1)
+    res = {
+        "metric": "sparse decode step GB/s (% HBM peak), Mistral-7B-shaped ragged batch, 64 fused steps at 50%",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": nsteps, "warmup": 0,
+        "ms_per_step": round(seq_total / nsteps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16 in, f32 accumulate", "data": "synthetic (seeded)",
+        "config": {"workload": "mistral_ragged_append: B=16, 32 q / 8 kv heads, head_dim 128, lengths "
+                               "uniform in [4096, 32768], keep 64; 64 mustafar_decode_step calls back to back",
+                   "batch": B, "q_heads": Hq, "kv_heads": Hkv, "seq_lens": seq0.tolist(), "keep": keep},
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(total_bytes / nsteps),
+                     "avg_launch_us": round(seq_total / nsteps * 1e6, 2)},
+        "cpu_baseline": {"value": round(last_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": nth,
+                         "kind": "oracle", "hardware_concurrency": hw, "nproc": nproc,
+                         "prefill_compress_s": round(cpu_pre, 3), "append_128_steps_s": round(cpu_app, 3),
+                         "sample": f"prefill prune + compress of the batch's K and V, 128 appends, and one "
+                                   f"decode step over all {B * Hq} (batch, q head) pairs ({cpu_s:.2f} s)"},
+        "extra": {"per_step_gbs": {"min": round(min(per_gbs), 1), "median": round(median(per_gbs), 1),
+                                   "max": round(max(per_gbs), 1)},
+                  "per_step_us_with_events": [round(t * 1e6, 2) for t in per],
+                  "decode_only_us_after_1gib_read": round(sparse_s * 1e6, 2),
+                  "dense_us_after_1gib_read": round(dense_s * 1e6, 2),
+                  "speedup_vs_dense": round(dense_s / sparse_s, 3),
+                  "parity": {"caches_bit_exact": bool(exact), "max_abs": err, "rel_l2": rel}},
+    }
+    print(json.dumps(res), flush=True)
+    return 0 if ok else 3
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +477,9 @@ def main() -> int:
                     help="skip the per-head keep, channel-wise and 2:4 measurements")
     ap.add_argument("--stack-sweep", action="store_true",
                     help="instead of the benchmark: the 32-layer stack batch x length sweep")
+    ap.add_argument("--workload", default="llama3_8b_layer",
+                    choices=["llama3_8b_layer", "llama2_7b_layer", "mistral_ragged_append"],
+                    help="llama3_8b_layer (default): the headline layer; the others: their own JSON line")
     ap.add_argument("--layers", type=int, default=3,
                     help="layer caches the steps take turns over (>= 2 keeps them out of the LLC)")
     args = ap.parse_args()
@@ -210,6 +490,10 @@ def main() -> int:
         return 2
     if args.stack_sweep:
         return stack_sweep(args)
+    if args.workload == "llama2_7b_layer":
+        return bench_llama2_layer(args)
+    if args.workload == "mistral_ragged_append":
+        return bench_ragged_append(args)
 
     import numpy as np
     import torch
@@ -502,41 +786,71 @@ def main() -> int:
                 f"({bsz * Hkv * T0 * 512 / dense[bsz] / 1e9:.0f} GB/s)")
     del flush
 
-    # ---- parity of the last decode step and the CPU oracle on that full step
+    # ---- the CPU oracle on the same workload: parity of the whole layer and the baseline.
+    # The oracle compresses layer 0's prefill cache from the dense bits the GPU
+    # pruned (timed: the prefill prune + compress), grows it by its own append
+    # with every row the steps appended to layer 0, and attends the last step's
+    # query (timed: one decode step).  Its caches must equal the GPU's bit for
+    # bit and its output must match the GPU's within the attention tolerance;
+    # otherwise the line is printed and the run exits non-zero.
     cpu = None
     parity = None
+    parity_ok = True
     if not args.no_cpu_baseline:
         import oracle
         usk.decode_attn(q_last, kc, vc, seq_d, cap, scale, out, ws)
         torch.cuda.synchronize()
         L = int(seq_d[0].item())
-        sh = np.full(B, L, np.int32)
-
-        def host_copy(c):
-            bm, vals, toff = c.views()
-            h = oracle.Compressed(B, Hkv, cap, d, keep)
-            h.bitmaps[...] = bm.cpu().numpy().view(np.uint64)
-            h.values[...] = vals.cpu().numpy().view(np.uint16)
-            h.tile_off[...] = toff.cpu().numpy().view(np.uint32)
-            return h
-
-        kh, vh = host_copy(kc), host_copy(vc)
-        nthreads = min(16, oracle.hardware_threads())
-        log(f"CPU oracle: one full decode step ({B * Hq} (batch, q head) pairs, {L} tokens) "
-            f"on {nthreads} threads")
+        hw = oracle.hardware_threads()
+        nproc = len(os.sched_getaffinity(0))
+        # the GPU machine grants each GPU a 16-core share of the host, whatever the host shows
+        nthreads = max(1, min(16, nproc))
+        log(f"CPU oracle: hardware_concurrency={hw}, nproc={nproc}, using {nthreads} threads")
+        K0c, V0c = K0[:, :, :T0].cpu(), V0[:, :, :T0].cpu()
+        seq0 = np.full(B, T0, np.int32)
         c0 = time.perf_counter()
-        ref = oracle.attention_compressed(q_last.cpu(), kh, vh, sh, scale, nthreads=nthreads)
+        ko = oracle.compress(K0c, seq0, keep, cap, nthreads=nthreads)
+        vo = oracle.compress(V0c, seq0, keep, cap, nthreads=nthreads)
+        cpu_pre_s = time.perf_counter() - c0
+        del K0c, V0c
+        seq_o = seq0
+        for i in range(0, args.warmup + args.steps + sep_steps, NL):  # the steps that visited layer 0
+            seq_o, st = oracle.append_step(ko, vo, steps_in[i][0].cpu(), steps_in[i][1].cpu(), seq_o)
+            assert st == 0
+        assert int(seq_o[0]) == L, (seq_o, L)
+
+        def same(c, o):
+            bm, vals, toff = (t.cpu().numpy() for t in c.views())
+            nt = (L + 63) // 64 + 1
+            return (np.array_equal(bm.view(np.uint64)[:, :, :L], o.bitmaps[:, :, :L])
+                    and np.array_equal(vals.view(np.uint16)[:, :, :L * keep], o.values[:, :, :L * keep])
+                    and np.array_equal(toff.view(np.uint32)[:, :, :nt], o.tile_off[:, :, :nt]))
+
+        caches_exact = same(kc, ko) and same(vc, vo)
+        c0 = time.perf_counter()
+        ref = oracle.attention_compressed(q_last.cpu(), ko, vo, seq_o, scale, nthreads=nthreads)
         cpu_s = time.perf_counter() - c0
-        cpu_bytes = kc.used_bytes(sh) + vc.used_bytes(sh)
+        cpu_bytes = kc.used_bytes(seq_o) + vc.used_bytes(seq_o)
         got = out.float().cpu().numpy().astype(np.float64)
-        parity = {"max_abs": float(np.abs(got - ref).max()),
-                  "rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref))}
+        parity = {"caches_bit_exact": bool(caches_exact),
+                  "max_abs": float(np.abs(got - ref).max()),
+                  "rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
+                  "tolerance": {"max_abs": 1e-2, "rel_l2": 1e-3},
+                  "scope": f"layer 0 after its appended steps: all {B * Hkv} (batch, kv head) units' "
+                           f"key and value caches, all {B * Hq} outputs of one decode call"}
+        parity_ok = caches_exact and parity["max_abs"] <= 1e-2 and parity["rel_l2"] <= 1e-3
+        pre_bytes = dense_bytes0 + comp_bytes0
         cpu = {"value": round(cpu_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": nthreads,
-               "kind": "oracle",
+               "kind": "oracle", "hardware_concurrency": hw, "nproc": nproc,
+               "prefill_compress_s": round(cpu_pre_s, 3),
+               "prefill_compress_gbs_moved": round(pre_bytes / cpu_pre_s / 1e9, 3),
                "sample": f"one full decode step of the workload: attention for all {B * Hq} "
                          f"(batch, q head) pairs over the {L}-token compressed caches "
-                         f"({cpu_bytes} compressed bytes), {cpu_s:.2f} s wall"}
-        log(f"CPU oracle: {cpu_s:.2f} s ({cpu['value']} GB/s); GPU vs oracle max_abs="
+                         f"({cpu_bytes} compressed bytes), {cpu_s:.2f} s wall; and the prefill "
+                         f"prune + compress of the layer's {T0}-token key and value caches "
+                         f"({pre_bytes} bytes moved), {cpu_pre_s:.2f} s wall"}
+        log(f"CPU oracle: prefill compress {cpu_pre_s:.2f} s, decode step {cpu_s:.2f} s "
+            f"({cpu['value']} GB/s); caches bit-exact={caches_exact}; GPU vs oracle max_abs="
             f"{parity['max_abs']:.2e} rel_l2={parity['rel_l2']:.2e}")
 
     decode_s = median(kern_s)
@@ -598,6 +912,9 @@ def main() -> int:
             "pages_tokens_per_s_ratio_b8_vs_b6": 2.23,
         })
     print(json.dumps(res), flush=True)
+    if not parity_ok:
+        log("PARITY FAILURE: the GPU caches or output differ from the oracle's (see parity_last_step)")
+        return 3
     return 0
 
 
