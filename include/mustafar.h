@@ -31,8 +31,9 @@
  *   - head_dim must be 128.  Device pointers must be 16-byte aligned.
  *   - Lengths in seq_lens (device) are read by the kernels and clamped to
  *     [0, capacity]; the host cannot see them.
- *   - No global mutable state: calls on different streams and buffers may run
- *     concurrently from any thread.
+ *   - No global mutable state (except the device scratch array of
+ *     mustafar_decode_step_noalloc): calls on different streams and buffers may
+ *     run concurrently from any thread.
  */
 #ifndef MUSTAFAR_H_
 #define MUSTAFAR_H_
@@ -293,6 +294,33 @@ int mustafar_decode_step(const uint16_t *q, int32_t num_q_heads, const mustafar_
                          int32_t *seq_lens, uint32_t *status, int32_t max_seq_len, float scale,
                          int32_t splits, uint16_t *out, void *workspace, uint64_t workspace_bytes,
                          void *stream);
+
+/*
+ * mustafar_decode_step without a workspace, for callers that cannot allocate
+ * device memory around the call (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same operation, arguments (minus
+ * workspace and workspace_bytes), results bit for bit and errors as
+ * mustafar_decode_step; the call itself allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).
+ *
+ * The split partials go to a device array of the library,
+ * MUSTAFAR_NOALLOC_SCRATCH_BYTES long, one per device, held from the library's
+ * load on that device until the process ends.  A shape whose partials
+ * (batch * num_q_heads * splits * 528 bytes, splits as for splits = 0 when 0 is
+ * passed) exceed it returns MUSTAFAR_ENOSPACE and launches nothing.  Every call
+ * on one device shares that device's array: calls that overlap in time on one
+ * device (different streams, or threads without ordering) race and must be
+ * serialised by the caller; calls on one stream are ordered and safe.  The
+ * array's contents between calls are of no meaning (each call writes every
+ * partial it reads).  The first call on each device looks up the array's
+ * address once (hipGetSymbolAddress) and keeps it.
+ */
+#define MUSTAFAR_NOALLOC_SCRATCH_BYTES (8u << 20)
+int mustafar_decode_step_noalloc(const uint16_t *q, int32_t num_q_heads, const mustafar_kv_t *k,
+                                 const mustafar_kv_t *v, const uint16_t *k_new,
+                                 const uint16_t *v_new, int32_t *seq_lens, uint32_t *status,
+                                 int32_t max_seq_len, float scale, int32_t splits, uint16_t *out,
+                                 void *stream);
 
 /*
  * Channel-wise magnitude pruning, prefill (the channel-wise direction of the

@@ -1,7 +1,7 @@
 // Host-side driver for the sanitizer build of the library's C ABI: every
 // argument check, the byte accounting and the split / workspace sizing, run
-// under AddressSanitizer and UndefinedBehaviorSanitizer (api.hip built for the
-// host only, kernel launchers stubbed).  Only paths that return before a
+// under AddressSanitizer and UndefinedBehaviorSanitizer (api.hip's host side
+// built with them, kernel launchers stubbed).  Only paths that return before a
 // launch are taken: argument errors, and -- when no device is visible -- the
 // MUSTAFAR_ENODEV answer to otherwise valid calls.  Expected values are the
 // closed forms stated in include/mustafar.h.  Exit status 0 = every check held.
@@ -193,7 +193,15 @@ static void call_errors(bool have_device) {
                                nullptr) == MUSTAFAR_ENODEV);
     CHECK(mustafar_dense_decode_attn(q, 8, dense, dense, 2, 2, 128, 128, seq, 128, sc, 0, out, ws, wsb,
                                      nullptr) == MUSTAFAR_ENODEV);
+    CHECK(mustafar_decode_step_noalloc(q, 8, &k, &v, dense, dense, seq, status, 128, sc, 0, out,
+                                       nullptr) == MUSTAFAR_ENODEV);
   }
+  // the no-alloc step refuses partials beyond its scratch array before any device call
+  mustafar_kv_t kb = kv_of(256, 8, 38, 64), vb = kv_of(256, 8, 38, 64);
+  CHECK(mustafar_decode_step_noalloc(q, 64, &kb, &vb, dense, dense, seq, status, 64, sc, 0, out,
+                                     nullptr) == MUSTAFAR_ENOSPACE);
+  CHECK(mustafar_decode_step_noalloc(q, 8, &k, &v, nullptr, dense, seq, status, 128, sc, 0, out,
+                                     nullptr) == MUSTAFAR_EINVAL);
 }
 
 int main() {

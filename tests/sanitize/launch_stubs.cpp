@@ -1,5 +1,5 @@
 // Kernel launchers replaced by stubs for the host-side sanitizer build of the
-// library's C ABI (api.hip compiled for the host only).  The driver only takes
+// library's C ABI (api.hip with the sanitizers on its host side).  The driver only takes
 // paths that return before any launch; a stub that is reached reports it.
 #include <stdio.h>
 #include <stdlib.h>

@@ -32,7 +32,9 @@ EXPORTS = (
     "mustafar_decode_workspace_init", "mustafar_decode_attn", "mustafar_decode_attn_valu",
     "mustafar_decode_step", "mustafar_dense_decode_attn", "mustafar_probe_stream_read",
     "mustafar_prune_compress_24", "mustafar_decode_attn_24", "mustafar_prune_compress_channel",
+    "mustafar_decode_step_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class KVStruct(ctypes.Structure):
@@ -83,6 +85,8 @@ def lib() -> ctypes.CDLL:
                                                          I32, P, P, U64, P]),
             "mustafar_decode_step": (ctypes.c_int, [P, I32, KVP, KVP, P, P, P, P, I32, ctypes.c_float,
                                                     I32, P, P, U64, P]),
+            "mustafar_decode_step_noalloc": (ctypes.c_int, [P, I32, KVP, KVP, P, P, P, P, I32,
+                                                            ctypes.c_float, I32, P, P]),
             "mustafar_dense_decode_attn": (ctypes.c_int, [P, I32, P, P, I32, I32, I32, I64, P, I32,
                                                           ctypes.c_float, I32, P, P, U64, P]),
             "mustafar_probe_stream_read": (ctypes.c_int, [P, U64, P, P]),
@@ -265,6 +269,19 @@ def decode_step(q, k: CompressedKV, v: CompressedKV, k_new, v_new, seq_lens, max
         q.data_ptr(), q.shape[1], k.ref, v.ref, k_new.data_ptr(), v_new.data_ptr(),
         seq_lens.data_ptr(), _ptr(status), max_seq_len, scale, splits, out.data_ptr(),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def decode_step_noalloc(q, k: CompressedKV, v: CompressedKV, k_new, v_new, seq_lens,
+                        max_seq_len: int, scale: float, out, status=None, splits: int = 0,
+                        stream=None) -> None:
+    """decode_step without a workspace: the split partials go to the library's own
+    device scratch array (calls on one device must not overlap in time)."""
+    assert q.is_contiguous() and out.is_contiguous()
+    assert k_new.is_contiguous() and v_new.is_contiguous()
+    _check("mustafar_decode_step_noalloc", lib().mustafar_decode_step_noalloc(
+        q.data_ptr(), q.shape[1], k.ref, v.ref, k_new.data_ptr(), v_new.data_ptr(),
+        seq_lens.data_ptr(), _ptr(status), max_seq_len, scale, splits, out.data_ptr(),
+        _stream(stream)))
 
 
 def dense_decode_attn(q, k, v, seq_lens, max_seq_len: int, scale: float, out, workspace,

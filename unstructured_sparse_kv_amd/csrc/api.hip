@@ -4,12 +4,46 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 using namespace mustafar;
 
+// Split partials of mustafar_decode_step_noalloc: a file-scope device array, so
+// that the call allocates nothing.  Each device holds its own copy (from module
+// load until the process ends) at its own address.  In host code the name is a
+// host-side stand-in, never a device address: only the per-device pointer that
+// hipGetSymbolAddress returns (scratch_of_current_device) is ever passed on.
+static __device__ __align__(256) uint8_t scratch[MUSTAFAR_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up once per device (with that
+// device current) and kept.
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MUSTAFAR_ENODEV;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MUSTAFAR_EUNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MUSTAFAR_ELAUNCH;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MUSTAFAR_OK;
+}
 
 constexpr int kMaxSplits = 1024;
 constexpr int64_t kMaxCapacity = 1 << 24;
@@ -123,6 +157,10 @@ typedef hipError_t (*SparseLauncher)(const SparseDecodeArgs&, int, hipStream_t);
 
 // Decode over the compressed caches; with k_new / v_new (the fused step) the
 // split kernel first stores the new rows and the merge kernel advances seq_lens.
+// workspace == kUseScratch: the partials go to the library's scratch array
+// (workspace_bytes is then its size), looked up after the argument checks.
+void* const kUseScratch = reinterpret_cast<void*>(uintptr_t{256});
+
 int sparse_decode(SparseLauncher launch, const uint16_t* q, int32_t num_q_heads,
                   const mustafar_kv_t* k, const mustafar_kv_t* v, const int32_t* seq_lens,
                   int32_t max_seq_len, float scale, int32_t splits, uint16_t* out,
@@ -140,6 +178,7 @@ int sparse_decode(SparseLauncher launch, const uint16_t* q, int32_t num_q_heads,
                             out, workspace, workspace_bytes, seq_lens, &sp);
   if (rc) return rc;
   if ((rc = check_device())) return rc;
+  if (workspace == kUseScratch && (rc = scratch_of_current_device(&workspace))) return rc;
   a.q = q;
   a.Hq = num_q_heads;
   a.Hkv = k->num_kv_heads;
@@ -333,6 +372,17 @@ int mustafar_decode_step(const uint16_t* q, int32_t num_q_heads, const mustafar_
   if (status && !aligned4(status)) return MUSTAFAR_EINVAL;
   return sparse_decode(launch_decode_sparse, q, num_q_heads, k, v, seq_lens, max_seq_len, scale,
                        splits, out, workspace, workspace_bytes, stream, k_new, v_new, status);
+}
+
+int mustafar_decode_step_noalloc(const uint16_t* q, int32_t num_q_heads, const mustafar_kv_t* k,
+                                 const mustafar_kv_t* v, const uint16_t* k_new, const uint16_t* v_new,
+                                 int32_t* seq_lens, uint32_t* status, int32_t max_seq_len,
+                                 float scale, int32_t splits, uint16_t* out, void* stream) {
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return MUSTAFAR_EINVAL;
+  if (status && !aligned4(status)) return MUSTAFAR_EINVAL;
+  return sparse_decode(launch_decode_sparse, q, num_q_heads, k, v, seq_lens, max_seq_len, scale,
+                       splits, out, kUseScratch, MUSTAFAR_NOALLOC_SCRATCH_BYTES, stream, k_new,
+                       v_new, status);
 }
 
 int mustafar_dense_decode_attn(const uint16_t* q, int32_t num_q_heads, const uint16_t* k,
