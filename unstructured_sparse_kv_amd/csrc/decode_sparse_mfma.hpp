@@ -17,13 +17,14 @@
 //               from LDS, B = the G query heads as columns (registers), 4 row
 //               blocks x 4 channel blocks; lane l ends with head l%16 of rows
 //               16*mb + 4*(l/16) + i.
+//   value tile  walk the value bitmap into a zeroed channel-major tile
+//               V[c][t] in the same LDS buffer (row stride 144 B), while the
+//               score MFMAs run.
 //   softmax     tile_softmax.hpp: per head, online; with G <= 4 the scores
 //               are first compacted onto the lanes of the padding heads; the
 //               running reference max is raised (and the accumulators
 //               rescaled) only when a score exceeds it by more than 8 in log2
 //               units, so p <= 2^8; p to LDS as fp16 p[head][row].
-//   value tile  walk the value bitmap into a zeroed channel-major tile
-//               V[c][t] in the same LDS buffer (row stride 144 B).
 //   P.V         v_mfma_f32_16x16x32_f16: A = 16 channels x 32 rows of V,
 //               B = p[rows][heads]; accumulators out[channel][head] stay in
 //               registers for the whole split (8 channel blocks x 2 row blocks).
@@ -285,11 +286,11 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
       }
     }
 
-    // ---- online softmax (tile_softmax.hpp); p to LDS
-    tile_softmax<G>(cs, a.scale_log2, partial, nvalid, l16, grp, m, lsum, acc, p_lds);
-
-    // ---- value tile V[c][t] in the same buffer
-    wave_lds_sync();  // score reads of the key tile done; p written
+    // ---- value tile V[c][t] in the same buffer, walked while the score MFMAs
+    // run: a wave's LDS operations execute in order, so its stores land after
+    // the score operand reads (which cleared the buffer); only the compiler
+    // must keep the order
+    wave_lds_sync();
     if constexpr (PATCH) take_new(new_lds + C::kNewSide, vb, vrow);
     decode_side<NMAX, NK, false, kVRow>(
         vrs, vt0, vk, valid, partial, !kEvenExact || !(vt0 & 1u), vb, vrow, tile_base + 2u * lane,
@@ -297,7 +298,10 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
           if constexpr (PATCH) { uint4 t; take_new(new_lds + C::kNewSide, t, r); }
         });
     issue_v(nxt, vt0n);
-    wave_lds_sync();
+
+    // ---- online softmax (tile_softmax.hpp); p to LDS
+    tile_softmax<G>(cs, a.scale_log2, partial, nvalid, l16, grp, m, lsum, acc, p_lds);
+    wave_lds_sync();  // p and the value tile written
 
     // ---- P.V: 8 channel blocks x 2 row blocks
     const uint16_t* prow = p_lds + (l16 < (uint32_t)G ? l16 : (uint32_t)G) * 64 + 8 * grp;

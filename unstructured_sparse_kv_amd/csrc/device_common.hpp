@@ -93,6 +93,52 @@ __device__ __forceinline__ float wave_max(float x) {
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
+// Butterflies over lanes l and l ^ 32 (l ^ 16) with the gfx950 lane-swap
+// instructions, which run on the vector units (a __shfl_xor is an LDS
+// permute with an LDS round trip).  Swapping a register with itself leaves
+// x[l] in one result and x[l ^ 32] (x[l ^ 16]) in the other (checked on the
+// device), so an order-free combine of the two is the butterfly step.
+// The empty asm statement hides the two results from the code generator: it
+// otherwise treats a swap of two copies of one value as leaving both equal
+// and drops the combine (seen in the generated code after DPP row rotations).
+template <bool SWAP32>
+__device__ __forceinline__ void lane_swap_pair(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  unsigned r0, r1;
+  if constexpr (SWAP32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  asm volatile("" : "+v"(r0), "+v"(r1));
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float a, b;
+  lane_swap_pair<true>(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  float a, b;
+  lane_swap_pair<false>(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a, b;
+  lane_swap_pair<true>(x, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  float a, b;
+  lane_swap_pair<false>(x, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);

@@ -15,7 +15,8 @@
 // real scores (head l16 % 4, rows 16 (l16 / 4) + 4 grp + i) instead of 16 of
 // which most are padding; the scaling, exponentials and conversions then run a
 // quarter as often.  A head's maximum and sum are gathered over the four banks
-// with row_ror 4 and 8 and over the lane groups with xor 16 and 32.  With G = 8
+// with row_ror 4 and 8 and over the lane groups with xor 16 and 32 (lane swaps
+// on the vector units).  With G = 8
 // the same is done with one move per register (blocks 2 and 3 to the lanes of
 // columns 8-15), leaving 8 scores per lane.
 #pragma once
@@ -64,8 +65,7 @@ __device__ __forceinline__ void tile_softmax(const f32x4 (&cs)[4], float scale_l
     float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mt = fmaxf(mt, row_ror_f<4>(mt));
     mt = fmaxf(mt, row_ror_f<8>(mt));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = max_xor32(max_xor16(mt));
     // m, lsum belong to head l16 % 4: lanes l16 < G hold the heads' states
     if (__ballot(mt > m + kSoftmaxSlack) != 0ull) {
       const float mn = fmaxf(m, mt);
@@ -108,8 +108,7 @@ __device__ __forceinline__ void tile_softmax(const f32x4 (&cs)[4], float scale_l
 #pragma unroll
     for (int j = 0; j < 8; ++j) mt = fmaxf(mt, sv[j]);
     mt = fmaxf(mt, row_ror_f<8>(mt));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = max_xor32(max_xor16(mt));
     if (__ballot(mt > m + kSoftmaxSlack) != 0ull) {
       const float mn = fmaxf(m, mt);
       const float alpha = exp2_raw(m - mn);
@@ -148,8 +147,7 @@ __device__ __forceinline__ void tile_softmax(const f32x4 (&cs)[4], float scale_l
     float mt = ninf;
 #pragma unroll
     for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sv[j]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = max_xor32(max_xor16(mt));
     if (__ballot(mt > m + kSoftmaxSlack) != 0ull) {
       const float mn = fmaxf(m, mt);
       const float alpha = exp2_raw(m - mn);
@@ -187,9 +185,7 @@ __device__ __forceinline__ float tile_softmax_sum(float lsum) {
   } else if constexpr (G == 8) {
     lsum += row_ror_f<8>(lsum);
   }
-  lsum += __shfl_xor(lsum, 16, kWave);
-  lsum += __shfl_xor(lsum, 32, kWave);
-  return lsum;
+  return sum_xor32(sum_xor16(lsum));
 }
 
 }  // namespace mustafar
