@@ -87,6 +87,7 @@ struct PruneArgs {
   uint16_t* values;
   uint32_t* tile_off;
   KeepMap map;
+  int32_t tiles_per_unit, items;  // the per-lane kernel's flattened tile order
 };
 
 struct AppendArgs {
@@ -129,6 +130,28 @@ hipError_t ensure_lds_limit(int bytes) {
                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess && bit) configured.fetch_or(bit, std::memory_order_acq_rel);
   return e;
+}
+
+// Compute units of the current device, looked up once per device.
+inline hipError_t device_cu_count(int* cus) {
+  static std::atomic<int> cached[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  int c = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (c <= 0) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < 64) cached[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return hipSuccess;
 }
 
 // Workspace: the split partials, [batch][Hkv][splits][G][kPartStride] fp32.

@@ -71,12 +71,15 @@ __global__ __launch_bounds__(kPruneBlock) void prune_compress_kernel(PruneArgs a
   }
 }
 
-// Per-token pruning with one row per lane (select_lane.hpp): each wave takes
-// one 64-row tile of a (batch, kv head) unit.
-//   stage    the tile's 64 dense rows (16 KB, contiguous) are loaded with
-//            coalesced 16-byte loads and written to LDS (row stride 272 B);
-//            lane t then reads row t into registers (16 reads of 16 B; each
-//            quarter wave touches 64 distinct banks).
+// Per-token pruning with one row per lane (select_lane.hpp).  Each wave takes
+// 64-row tiles of the (batch, kv head) units in turn: tile i of the
+// unit-major order, then i + the number of waves in the grid, and so on.
+//   stage    the tile's 64 dense rows (16 KB, contiguous) arrive as sixteen
+//            coalesced 16-byte loads per lane into registers, issued while
+//            the wave still works on its previous tile; they are written to
+//            this wave's LDS tile (row stride 272 B) and lane t reads row t
+//            into registers (16 reads of 16 B; each quarter wave touches 64
+//            distinct banks).
 //   select   lane_select_row: the row's survivors as a 128-bit mask, with
 //            integer arithmetic on the lane's own keys only.
 //   bitmaps  lane t stores row t's two words (consecutive lanes, consecutive
@@ -85,36 +88,42 @@ __global__ __launch_bounds__(kPruneBlock) void prune_compress_kernel(PruneArgs a
 //            values from its staged row (one 2-byte LDS read per kept value,
 //            in channel order), then writes the packed row back to the LDS
 //            tile at t * keep values; the tile's packed values (one contiguous
-//            run of n * keep values) are copied out with coalesced stores.
-// Grid (ceil(tiles / 4), units); units beyond gridDim.y in steps of gridDim.y.
+//            run of n * keep values, 16-byte aligned) are copied out with
+//            coalesced 16-byte stores.
+// The grid holds at most as many blocks as the chip keeps resident (two per
+// CU), so that every wave works through several tiles and its loads overlap
+// its own arithmetic.
 constexpr int kLaneRow = 272;           // staged row: 256 B + 16 B
 constexpr int kLaneWaves = 4;
 constexpr int kLaneBlock = kLaneWaves * kWave;
 constexpr int kLaneTileBytes = kTile * kLaneRow;
+constexpr int kLaneBlocksPerCu = 2;     // LDS: 2 x 4 x 17 KB of the CU's 160 KB
 
 // Gathers the values of the set bits of bm (channel order) from the lane's
-// staged row at LDS byte offset `row` into p (value 2i in the low half of
-// p[i], value 2i + 1 in the high half); bm holds exactly `keep` set bits.
-__device__ __forceinline__ void gather_kept(const uint32_t (&bm)[4], int keep, uint32_t row,
-                                            const char* lds, uint32_t (&p)[64]) {
-  // empty words compacted away; each kept word carries the byte offset of its channel 0
+// staged row at LDS address `row` into p (value 2i in the low half of p[i],
+// value 2i + 1 in the high half); bm holds exactly `keep` set bits.
+__device__ __forceinline__ void gather_kept(const uint32_t (&bm)[4], int keep, const char* row,
+                                            uint32_t (&p)[64]) {
+  // empty words compacted away; each kept word carries the address of its channel 0
   uint32_t cw[4] = {bm[0], bm[1], bm[2], bm[3]};
-  uint32_t cb[4] = {row, row + 64u, row + 128u, row + 192u};
+  const char* cb[4] = {row, row + 64, row + 128, row + 192};
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       const bool sw = (cw[j] == 0u) && (cw[j + 1] != 0u);
-      const uint32_t w = cw[j], b = cb[j];
+      const uint32_t w = cw[j];
+      const char* b = cb[j];
       cw[j] = sw ? cw[j + 1] : cw[j];
       cb[j] = sw ? cb[j + 1] : cb[j];
       cw[j + 1] = sw ? w : cw[j + 1];
       cb[j + 1] = sw ? b : cb[j + 1];
     }
   }
-  uint32_t cur = cw[0], b0 = cb[0], n1 = cw[1], b1 = cb[1], n2 = cw[2], b2 = cb[2], n3 = cw[3], b3 = cb[3];
+  uint32_t cur = cw[0], n1 = cw[1], n2 = cw[2], n3 = cw[3];
+  const char *b0 = cb[0], *b1 = cb[1], *b2 = cb[2], *b3 = cb[3];
   auto step = [&](int i) {
-    const uint32_t v = *reinterpret_cast<const uint16_t*>(lds + b0 + 2u * (uint32_t)__builtin_ctz(cur));
+    const uint32_t v = *reinterpret_cast<const uint16_t*>(b0 + 2u * (uint32_t)__builtin_ctz(cur));
     p[i >> 1] = (i & 1) ? (p[i >> 1] | (v << 16)) : v;
     cur &= cur - 1u;
     const bool z = (cur == 0u);
@@ -139,87 +148,136 @@ __device__ __forceinline__ void gather_kept(const uint32_t (&bm)[4], int keep, u
   }
 }
 
-__global__ __launch_bounds__(kLaneBlock) void prune_lane_kernel(PruneArgs a) {
+// One tile of the flattened unit-major order.  n <= 0: no row of it is inside
+// its sequence.
+struct LaneTile {
+  int unit, b, h, tile, t0, n, T;
+};
+
+__device__ __forceinline__ LaneTile lane_tile(const PruneArgs& a, const int32_t* __restrict__ seq_lens,
+                                              int item) {
+  LaneTile t;
+  t.unit = wave_uniform(item / a.tiles_per_unit);
+  t.tile = item - t.unit * a.tiles_per_unit;
+  t.b = t.unit / a.H;
+  t.h = t.unit - t.b * a.H;
+  int T = seq_lens[t.b];
+  t.T = T < 0 ? 0 : (T > a.rows_per_unit ? a.rows_per_unit : T);
+  t.t0 = t.tile * kTile;
+  t.n = min(kTile, t.T - t.t0);
+  return t;
+}
+
+// The 16 KB of tile t's rows, chunk c = 64 j + lane (row c / 16, bytes
+// 16 (c % 16)) into r[j]; rows past the tile's n (all of them when n <= 0 or
+// when `live` is false) read as zero without touching memory.
+__device__ __forceinline__ void lane_fetch(const PruneArgs& a, const LaneTile& t, bool live,
+                                           uint32_t lane, uint4 (&r)[16]) {
+  const uint32_t rows = live && t.n > 0 ? (uint32_t)t.n : 0u;
+  const auto src = make_rsrc(a.dense + ((int64_t)t.unit * a.t_stride + t.t0) * kHeadDim,
+                             rows * (uint32_t)(2 * kHeadDim));
+#pragma unroll
+  for (int j = 0; j < 16; ++j) r[j] = buf_load16(src, 16u * (64u * (uint32_t)j + lane));
+}
+
+// seq_lens (a copy of a.seq_lens) as a restrict argument: the kernel never
+// writes it, so its loads can go through the scalar unit.
+__global__ __launch_bounds__(kLaneBlock) void prune_lane_kernel(PruneArgs a,
+                                                               const int32_t* __restrict__ seq_lens) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr uint32_t kMapAt = offsetof(PruneArgs, map);
   const uint32_t lane = lane_id();
   const int wave = wave_uniform((int)(threadIdx.x / kWave));
-  const int tile = blockIdx.x * kLaneWaves + wave;
+  const int nwaves = (int)gridDim.x * kLaneWaves;
   const int ntoff = a.cap / kTile + 1;
-  const uint32_t buf = (uint32_t)(wave * kLaneTileBytes);  // this wave's LDS tile
-  for (int unit = blockIdx.y; unit < a.units; unit += gridDim.y) {
-    const int b = unit / a.H, h = unit - b * a.H;
-    const int keep = keep_of(a.map, kMapAt, h);
-    int T = a.seq_lens[b];
-    T = T < 0 ? 0 : (T > a.rows_per_unit ? a.rows_per_unit : T);
-    uint32_t* toff = a.tile_off + (int64_t)unit * ntoff;
-    if (tile == 0 && lane == 0 && T == 0) toff[0] = 0;
-    const int t0 = tile * kTile;
-    if (t0 >= T) continue;
-    const int n = min(kTile, T - t0);
-    if (lane == 0) {
-      toff[tile] = (uint32_t)(t0 * keep);
-      if (t0 + n == T) toff[(T + kTile - 1) / kTile] = (uint32_t)(T * keep);
+  char* const tl = smem + wave * kLaneTileBytes;  // this wave's LDS tile
+  int item = (int)blockIdx.x * kLaneWaves + wave;
+  if (item >= a.items) return;
+  LaneTile cur = lane_tile(a, seq_lens, item);
+  uint4 r[16];
+  lane_fetch(a, cur, true, lane, r);
+  for (;;) {
+    // r: the rows of tile `item`
+    const int next = item + nwaves;
+    const bool more = next < a.items;
+    uint32_t* toff = a.tile_off + (int64_t)cur.unit * ntoff;
+    if (cur.tile == 0 && lane == 0 && cur.T == 0) toff[0] = 0;
+    const int keep = keep_of(a.map, kMapAt, cur.h);
+    const int n = cur.n, t0 = cur.t0;
+    if (n > 0) {
+      if (lane == 0) {
+        toff[cur.tile] = (uint32_t)(t0 * keep);
+        if (t0 + n == cur.T) toff[(cur.T + kTile - 1) / kTile] = (uint32_t)(cur.T * keep);
+      }
+      // ---- stage (the previous tile's copy-out reads of the LDS tile are
+      // done: this wave's LDS operations run in order)
+      wave_lds_sync();
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t c = 64u * (uint32_t)j + lane;
+        *reinterpret_cast<uint4*>(tl + (c >> 4) * kLaneRow + 16u * (c & 15u)) = r[j];
+      }
     }
+    // the next tile's loads, in flight while this one is processed
+    const LaneTile nx = lane_tile(a, seq_lens, more ? next : item);
+    lane_fetch(a, nx, more, lane, r);
+    if (n > 0) {
+      wave_lds_sync();
+      uint32_t x[64];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4*>(tl + lane * kLaneRow + 16u * (uint32_t)j);
+        x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
+      }
 
-    // ---- stage: chunk c = 64 j + lane of the tile is row c / 16, bytes 16 (c % 16)
-    const auto src = make_rsrc(a.dense + ((int64_t)unit * a.t_stride + t0) * kHeadDim,
-                               (uint32_t)n * (uint32_t)(2 * kHeadDim));
-    wave_lds_sync();  // the previous unit's reads of this wave's tile are done
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t c = 64u * (uint32_t)j + lane;
-      const uint4 v = buf_load16(src, 16u * c);
-      *reinterpret_cast<uint4*>(smem + buf + (c >> 4) * kLaneRow + 16u * (c & 15u)) = v;
-    }
-    wave_lds_sync();
-    uint32_t x[64];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(smem + buf + lane * kLaneRow + 16u * (uint32_t)j);
-      x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
-    }
+      // ---- select; lanes past the end take the lowest `keep` channels (never stored)
+      uint32_t bm[4];
+      lane_select_row(x, (uint32_t)keep, bm);
+      if ((int)lane >= n) {
+        bm[0] = bm[1] = bm[2] = bm[3] = ~0u;
+        keep_lowest128(bm, (uint32_t)keep);
+      }
+      if ((int)lane < n)
+        *reinterpret_cast<uint4*>(a.bitmaps + ((int64_t)cur.unit * a.cap + t0 + lane) * 2) =
+            make_uint4(bm[0], bm[1], bm[2], bm[3]);
 
-    // ---- select; lanes past the end take the lowest `keep` channels (never stored)
-    uint32_t bm[4];
-    lane_select_row(x, (uint32_t)keep, bm);
-    if ((int)lane >= n) {
-      bm[0] = bm[1] = bm[2] = bm[3] = ~0u;
-      keep_lowest128(bm, (uint32_t)keep);
-    }
-    if ((int)lane < n)
-      *reinterpret_cast<uint4*>(a.bitmaps + ((int64_t)unit * a.cap + t0 + lane) * 2) =
-          make_uint4(bm[0], bm[1], bm[2], bm[3]);
-
-    // ---- pack
-    uint32_t p[64];
+      // ---- pack
+      uint32_t p[64];
 #pragma unroll
-    for (int j = 0; j < 64; ++j) p[j] = 0u;
-    gather_kept(bm, keep, buf + lane * kLaneRow, smem, p);
-    // the packed rows back to back in the same LDS tile (this wave's gathers
-    // are done: its LDS operations run in order)
-    wave_lds_sync();
-    const uint32_t o = lane * (uint32_t)keep;  // first value of row `lane` in the packed tile
-    if ((keep & 1) == 0) {
+      for (int j = 0; j < 64; ++j) p[j] = 0u;
+      gather_kept(bm, keep, tl + lane * kLaneRow, p);
+      // the packed rows back to back in the same LDS tile (this wave's gathers
+      // are done: its LDS operations run in order)
+      wave_lds_sync();
+      const uint32_t o = lane * (uint32_t)keep;  // first value of row `lane` in the packed tile
+      if ((keep & 1) == 0) {
 #pragma unroll
-      for (int j = 0; j < 64; ++j)
-        if (2 * j < keep) *reinterpret_cast<uint32_t*>(smem + buf + 2u * o + 4u * j) = p[j];
-    } else {
-      // odd keep: rows of odd lanes start at an odd value; write value by value
+        for (int j = 0; j < 64; ++j)
+          if (2 * j < keep) *reinterpret_cast<uint32_t*>(tl + 2u * o + 4u * j) = p[j];
+      } else {
+        // odd keep: rows of odd lanes start at an odd value; write value by value
 #pragma clang loop unroll(full)
-      for (int i = 0; i < 128; ++i)
-        if (i < keep)
-          *reinterpret_cast<uint16_t*>(smem + buf + 2u * (o + i)) =
-              (uint16_t)((i & 1) ? (p[i >> 1] >> 16) : p[i >> 1]);
+        for (int i = 0; i < 128; ++i)
+          if (i < keep)
+            *reinterpret_cast<uint16_t*>(tl + 2u * (o + i)) =
+                (uint16_t)((i & 1) ? (p[i >> 1] >> 16) : p[i >> 1]);
+      }
+      wave_lds_sync();
+      // coalesced copy-out of the n * keep values: 16-byte pieces, then at most
+      // seven single values (the run starts 16-byte aligned: 64 * keep * 2 bytes
+      // per tile, regions of capacity * keep values, capacity a multiple of 64)
+      char* dst = reinterpret_cast<char*>(a.values + region_of(a.map, kMapAt, cur.b, cur.h, a.cap) +
+                                          (int64_t)t0 * keep);
+      const uint32_t bytes = (uint32_t)(n * keep) * 2u;
+      for (uint32_t c = lane; c < bytes / 16u; c += kWave)
+        *reinterpret_cast<uint4*>(dst + 16u * c) = *reinterpret_cast<const uint4*>(tl + 16u * c);
+      const uint32_t tail = (bytes & ~15u) + 2u * lane;
+      if (tail < bytes)
+        *reinterpret_cast<uint16_t*>(dst + tail) = *reinterpret_cast<const uint16_t*>(tl + tail);
     }
-    wave_lds_sync();
-    // coalesced copy-out of n * keep values (whole dwords, then a last half)
-    uint16_t* dst = a.values + region_of(a.map, kMapAt, b, h, a.cap) + (int64_t)t0 * keep;
-    const uint32_t total = (uint32_t)(n * keep);
-    for (uint32_t d = lane; d < total / 2u; d += kWave)
-      reinterpret_cast<uint32_t*>(dst)[d] = *reinterpret_cast<const uint32_t*>(smem + buf + 4u * d);
-    if ((total & 1u) && lane == 0)
-      dst[total - 1u] = *reinterpret_cast<const uint16_t*>(smem + buf + 2u * (total - 1u));
+    if (!more) break;
+    item = next;
+    cur = nx;
   }
 }
 
@@ -428,8 +486,17 @@ hipError_t launch_prune_compress(const mustafar_kv_t& d, const KeepMap& map, con
     constexpr int lds = kLaneWaves * kLaneTileBytes;
     hipError_t e = ensure_lds_limit<&prune_lane_kernel>(lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prune_lane_kernel, dim3((unsigned)((tiles + kLaneWaves - 1) / kLaneWaves), gy),
-                       dim3(kLaneBlock), lds, stream, a);
+    int cus = 0;
+    e = device_cu_count(&cus);
+    if (e != hipSuccess) return e;
+    const int64_t items = units * tiles;
+    if (items > INT32_MAX) return hipErrorInvalidValue;
+    a.tiles_per_unit = (int32_t)tiles;
+    a.items = (int32_t)items;
+    const int64_t want = (items + kLaneWaves - 1) / kLaneWaves;
+    const int64_t resident = (int64_t)cus * kLaneBlocksPerCu;
+    hipLaunchKernelGGL(prune_lane_kernel, dim3((unsigned)(want < resident ? want : resident)),
+                       dim3(kLaneBlock), lds, stream, a, seq_lens);
   }
   return hipGetLastError();
 }
