@@ -101,8 +101,12 @@ constexpr int kLaneBlocksPerCu = 2;     // LDS: 2 x 4 x 17 KB of the CU's 160 KB
 
 // Gathers the values of the set bits of bm (channel order) from the lane's
 // staged row at LDS address `row` into p (value 2i in the low half of p[i],
-// value 2i + 1 in the high half); bm holds exactly `keep` set bits.
-__device__ __forceinline__ void gather_kept(const uint32_t (&bm)[4], int keep, const char* row,
+// value 2i + 1 in the high half), `steps` (wave-uniform) of them.  Without
+// SPARE, bm holds at least `steps` set bits; with it, a lane whose bits run
+// out reads channel 31 of its last word for the remaining steps (values never
+// used).
+template <bool SPARE>
+__device__ __forceinline__ void gather_kept(const uint32_t (&bm)[4], int steps, const char* row,
                                             uint32_t (&p)[64]) {
   // empty words compacted away; each kept word carries the address of its channel 0
   uint32_t cw[4] = {bm[0], bm[1], bm[2], bm[3]};
@@ -123,7 +127,8 @@ __device__ __forceinline__ void gather_kept(const uint32_t (&bm)[4], int keep, c
   uint32_t cur = cw[0], n1 = cw[1], n2 = cw[2], n3 = cw[3];
   const char *b0 = cb[0], *b1 = cb[1], *b2 = cb[2], *b3 = cb[3];
   auto step = [&](int i) {
-    const uint32_t v = *reinterpret_cast<const uint16_t*>(b0 + 2u * (uint32_t)__builtin_ctz(cur));
+    const uint32_t v = *reinterpret_cast<const uint16_t*>(
+        b0 + 2u * (uint32_t)__builtin_ctz(SPARE ? (cur | 0x80000000u) : cur));
     p[i >> 1] = (i & 1) ? (p[i >> 1] | (v << 16)) : v;
     cur &= cur - 1u;
     const bool z = (cur == 0u);
@@ -137,15 +142,49 @@ __device__ __forceinline__ void gather_kept(const uint32_t (&bm)[4], int keep, c
   constexpr int kChunk = 8;
 #pragma clang loop unroll(full)
   for (int i0 = 0; i0 < 128; i0 += kChunk) {
-    if (i0 + kChunk <= keep) {
+    if (i0 + kChunk <= steps) {
 #pragma clang loop unroll(full)
       for (int j = 0; j < kChunk; ++j) step(i0 + j);
-    } else if (i0 < keep) {
+    } else if (i0 < steps) {
 #pragma clang loop unroll(full)
       for (int j = 0; j < kChunk; ++j)
-        if (i0 + j < keep) step(i0 + j);
+        if (i0 + j < steps) step(i0 + j);
     }
   }
+}
+
+// 64 x 64 bit transpose across the wave: lane l holds row l as the 64-bit
+// value (w1:w0); afterwards bit j of lane l is what bit l of lane j was.  The
+// usual recursive block swap: at distance d = 32, 16, 8, 4, 2, 1 a lane
+// without bit d exchanges the columns with bit d set for its partner's
+// (lane l ^ d) columns without it.  For d < 32 each 32-bit word is done on its
+// own: the lower lane takes (P << d) in the positions with bit d set, the
+// upper one (P >> d) in those without, as a byte permute (d = 16, 8) or a
+// rotate and a bit-field insert (d = 4, 2, 1) with per-lane selectors.
+__device__ __forceinline__ void wave_transpose64(uint32_t& w0, uint32_t& w1, uint32_t lane) {
+  {
+    const uint32_t p0 = (uint32_t)__shfl_xor((int)w0, 32, kWave), p1 = (uint32_t)__shfl_xor((int)w1, 32, kWave);
+    if (lane & 32u) w0 = p1; else w1 = p0;
+  }
+  auto bytes = [&](uint32_t& w, int d, uint32_t sel) {
+    const uint32_t pw = (uint32_t)__shfl_xor((int)w, d, kWave);
+    w = byte_perm(pw, w, sel);
+  };
+  auto bits = [&](uint32_t& w, int d, uint32_t rot, uint32_t mask) {
+    const uint32_t pw = (uint32_t)__shfl_xor((int)w, d, kWave);
+    const uint32_t q = __builtin_amdgcn_alignbit(pw, pw, rot);  // rotate right
+    w = (q & mask) | (w & ~mask);
+  };
+  const uint32_t s16 = (lane & 16u) ? 0x03020706u : 0x05040100u;
+  const uint32_t s8 = (lane & 8u) ? 0x03070105u : 0x06020400u;
+  const uint32_t r4 = (lane & 4u) ? 4u : 28u, m4 = (lane & 4u) ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
+  const uint32_t r2 = (lane & 2u) ? 2u : 30u, m2 = (lane & 2u) ? 0x33333333u : 0xCCCCCCCCu;
+  const uint32_t r1 = (lane & 1u) ? 1u : 31u, m1 = (lane & 1u) ? 0x55555555u : 0xAAAAAAAAu;
+  bytes(w0, 16, s16); bytes(w1, 16, s16);
+  bytes(w0, 8, s8);   bytes(w1, 8, s8);
+  bits(w0, 4, r4, m4); bits(w1, 4, r4, m4);
+  bits(w0, 2, r2, m2); bits(w1, 2, r2, m2);
+  bits(w0, 1, r1, m1); bits(w1, 1, r1, m1);
 }
 
 // One tile of the flattened unit-major order.  n <= 0: no row of it is inside
@@ -182,6 +221,16 @@ __device__ __forceinline__ void lane_fetch(const PruneArgs& a, const LaneTile& t
 
 // seq_lens (a copy of a.seq_lens) as a restrict argument: the kernel never
 // writes it, so its loads can go through the scalar unit.
+// CHANNEL: the channel-wise rule for full tiles (the map then holds one even
+// keep for every head): lane l reads channels 2l, 2l + 1 of the 64 staged rows
+// (consecutive lanes, consecutive dwords of a row), lane_select_columns marks
+// each channel's keep/2 kept rows, two 64 x 64 transposes across the wave turn
+// the two column masks into row masks, and a bit shuffle interleaves them into
+// row t's bitmap on lane t.  Rows then hold different numbers of values: each
+// row's run starts at the prefix sum of the earlier rows' counts, and the walk
+// takes as many steps as the longest row.  A partial tile takes the per-token
+// rule.
+template <bool CHANNEL>
 __global__ __launch_bounds__(kLaneBlock) void prune_lane_kernel(PruneArgs a,
                                                                const int32_t* __restrict__ seq_lens) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -223,54 +272,92 @@ __global__ __launch_bounds__(kLaneBlock) void prune_lane_kernel(PruneArgs a,
     lane_fetch(a, nx, more, lane, r);
     if (n > 0) {
       wave_lds_sync();
-      uint32_t x[64];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(tl + lane * kLaneRow + 16u * (uint32_t)j);
-        x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
-      }
-
-      // ---- select; lanes past the end take the lowest `keep` channels (never stored)
       uint32_t bm[4];
-      lane_select_row(x, (uint32_t)keep, bm);
-      if ((int)lane >= n) {
-        bm[0] = bm[1] = bm[2] = bm[3] = ~0u;
-        keep_lowest128(bm, (uint32_t)keep);
+      int steps = keep;       // walk length (wave-uniform)
+      uint32_t count = keep;  // this row's kept values
+      uint32_t start = lane * (uint32_t)keep;  // its first value in the packed tile
+      const bool by_channel = CHANNEL && n == kTile;
+      if (by_channel) {
+        uint32_t y[64];
+#pragma unroll
+        for (int r = 0; r < 64; ++r) y[r] = *reinterpret_cast<const uint32_t*>(tl + r * kLaneRow + 4u * lane);
+        uint32_t lo[2], hi[2];
+        lane_select_columns(y, (uint32_t)keep / 2u, lo, hi);
+        wave_transpose64(lo[0], lo[1], lane);
+        wave_transpose64(hi[0], hi[1], lane);
+        bm[0] = shuffle32(byte_perm(hi[0], lo[0], 0x05040100u));
+        bm[1] = shuffle32(byte_perm(hi[0], lo[0], 0x07060302u));
+        bm[2] = shuffle32(byte_perm(hi[1], lo[1], 0x05040100u));
+        bm[3] = shuffle32(byte_perm(hi[1], lo[1], 0x07060302u));
+        count = popc32(bm[0]) + popc32(bm[1]) + popc32(bm[2]) + popc32(bm[3]);
+        start = wave_excl_scan(count);
+        steps = (int)wave_uniform(wave_max_u32(count));
+      } else {
+        uint32_t x[64];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint4 v = *reinterpret_cast<const uint4*>(tl + lane * kLaneRow + 16u * (uint32_t)j);
+          x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
+        }
+        // lanes past the end take the lowest `keep` channels (never stored)
+        lane_select_row(x, (uint32_t)keep, bm);
+        if ((int)lane >= n) {
+          bm[0] = bm[1] = bm[2] = bm[3] = ~0u;
+          keep_lowest128(bm, (uint32_t)keep);
+        }
       }
       if ((int)lane < n)
         *reinterpret_cast<uint4*>(a.bitmaps + ((int64_t)cur.unit * a.cap + t0 + lane) * 2) =
             make_uint4(bm[0], bm[1], bm[2], bm[3]);
 
       // ---- pack
-      uint32_t p[64];
+      uint32_t p[64];  // (zeroed: left undefined, the unrolled walk's paths cost copies)
 #pragma unroll
       for (int j = 0; j < 64; ++j) p[j] = 0u;
-      gather_kept(bm, keep, tl + lane * kLaneRow, p);
+      gather_kept<CHANNEL>(bm, steps, tl + lane * kLaneRow, p);
       // the packed rows back to back in the same LDS tile (this wave's gathers
       // are done: its LDS operations run in order)
       wave_lds_sync();
-      const uint32_t o = lane * (uint32_t)keep;  // first value of row `lane` in the packed tile
-      if ((keep & 1) == 0) {
-#pragma unroll
-        for (int j = 0; j < 64; ++j)
-          if (2 * j < keep) *reinterpret_cast<uint32_t*>(tl + 2u * o + 4u * j) = p[j];
+      char* const prow = tl + 2u * start;  // packed row `lane`
+      constexpr int kChunk = 8;
+      if (!by_channel && (keep & 1) == 0) {
+        const int nd = keep / 2;
+#pragma clang loop unroll(full)
+        for (int j0 = 0; j0 < 64; j0 += kChunk) {
+          if (j0 + kChunk <= nd) {
+#pragma clang loop unroll(full)
+            for (int j = j0; j < j0 + kChunk; ++j) *reinterpret_cast<uint32_t*>(prow + 4 * j) = p[j];
+          } else if (j0 < nd) {
+#pragma clang loop unroll(full)
+            for (int j = j0; j < j0 + kChunk; ++j)
+              if (j < nd) *reinterpret_cast<uint32_t*>(prow + 4 * j) = p[j];
+          }
+        }
       } else {
-        // odd keep: rows of odd lanes start at an odd value; write value by value
+        // rows that start at an odd value: value by value (`count` of them)
 #pragma clang loop unroll(full)
         for (int i = 0; i < 128; ++i)
-          if (i < keep)
-            *reinterpret_cast<uint16_t*>(tl + 2u * (o + i)) =
-                (uint16_t)((i & 1) ? (p[i >> 1] >> 16) : p[i >> 1]);
+          if (i < steps && (uint32_t)i < count)
+            *reinterpret_cast<uint16_t*>(prow + 2 * i) = (uint16_t)((i & 1) ? (p[i >> 1] >> 16) : p[i >> 1]);
       }
       wave_lds_sync();
-      // coalesced copy-out of the n * keep values: 16-byte pieces, then at most
-      // seven single values (the run starts 16-byte aligned: 64 * keep * 2 bytes
-      // per tile, regions of capacity * keep values, capacity a multiple of 64)
+      // coalesced copy-out of the n * keep values: 16-byte pieces in groups of
+      // four (four LDS reads, then four stores: the reads stay inside this
+      // wave's tile, the stores past the last whole piece fall outside the
+      // buffer range and are dropped), then at most seven single values.  The
+      // run starts 16-byte aligned: 64 * keep * 2 bytes per tile, regions of
+      // capacity * keep values, capacity a multiple of 64.
       char* dst = reinterpret_cast<char*>(a.values + region_of(a.map, kMapAt, cur.b, cur.h, a.cap) +
                                           (int64_t)t0 * keep);
       const uint32_t bytes = (uint32_t)(n * keep) * 2u;
-      for (uint32_t c = lane; c < bytes / 16u; c += kWave)
-        *reinterpret_cast<uint4*>(dst + 16u * c) = *reinterpret_cast<const uint4*>(tl + 16u * c);
+      const auto out = make_rsrc(dst, bytes & ~15u);
+      for (uint32_t c0 = 0; c0 < bytes / 16u; c0 += 4u * kWave) {
+        uint4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const uint4*>(tl + 16u * (c0 + 64u * k + lane));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) buf_store16(out, 16u * (c0 + 64u * k + lane), v[k]);
+      }
       const uint32_t tail = (bytes & ~15u) + 2u * lane;
       if (tail < bytes)
         *reinterpret_cast<uint16_t*>(dst + tail) = *reinterpret_cast<const uint16_t*>(tl + tail);
@@ -329,107 +416,51 @@ __global__ __launch_bounds__(1024) void append_kernel(AppendArgs a) {
   }
 }
 
-// Channel-wise pruning (the channel-wise direction of the pages' pruning
-// variants, [README] "Part II"): in a full 64-row tile each channel keeps its
-// keep/2 entries of largest magnitude over the tile's rows, ties to the
-// earlier row, so the tile stores 64 * keep values; the rows of a final
-// partial tile are pruned per token to keep.
-//
-// One wave per (tile, unit); grid (tiles, units), units beyond gridDim.y in
-// steps of gridDim.y.  The tile is staged in LDS (row stride 260 B: a column
-// read by the 64 lanes touches every bank twice).  For a full tile lane t owns
-// row t: per channel, a ballot bisection over the 15 key bits finds the
-// (keep/2)-th largest key of the column, ties go to the lower lanes (earlier
-// rows), and each lane gathers its row's bits of the 128 channel ballots into
-// its bitmap words.  The kept values are packed row after row in LDS and
-// copied out with consecutive lanes on consecutive halves.  Every earlier tile
-// is full, so this tile's values start at 64 * keep * tile.
-constexpr int kChanRow = 130;  // staged row: 128 fp16 + 4 B
+}  // namespace
 
-__global__ __launch_bounds__(kWave) void prune_channel_kernel(PruneArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);            // [64][kChanRow]
-  uint16_t* packed = xs + kTile * kChanRow;                      // [64 * keep]
-  const uint32_t lane = lane_id();
-  const int tile = blockIdx.x;
-  const int keep = a.map.keep, kc = keep / 2;
-  const int ntoff = a.cap / kTile + 1;
-  for (int unit = blockIdx.y; unit < a.units; unit += gridDim.y) {
-    const int b = unit / a.H;
-    int T = a.seq_lens[b];
-    T = T < 0 ? 0 : (T > a.rows_per_unit ? a.rows_per_unit : T);
-    uint32_t* toff = a.tile_off + (int64_t)unit * ntoff;
-    if (tile == 0 && lane == 0 && T == 0) toff[0] = 0;
-    const int t0 = tile * kTile;
-    if (t0 >= T) continue;
-    const int n = min(kTile, T - t0);
-    const uint32_t v0 = (uint32_t)(t0 * keep);  // values before this tile
-    uint64_t* bm = a.bitmaps + ((int64_t)unit * a.cap + t0) * 2;
-    uint16_t* vals = a.values + (int64_t)unit * a.cap * keep + v0;
-    if (lane == 0) {
-      toff[tile] = v0;
-      if (t0 + n == T) toff[(T + kTile - 1) / kTile] = v0 + (uint32_t)(n * keep);
-    }
-    // stage the tile's rows (lane t copies row t)
-    const uint16_t* src = a.dense + ((int64_t)unit * a.t_stride + t0) * kHeadDim;
-    __syncthreads();  // the previous unit's reads of the staging area are done
-    if ((int)lane < n) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint4 c = *reinterpret_cast<const uint4*>(src + lane * kHeadDim + 8 * j);
-        uint32_t* d = reinterpret_cast<uint32_t*>(xs + lane * kChanRow + 8 * j);
-        d[0] = c.x; d[1] = c.y; d[2] = c.z; d[3] = c.w;
-      }
-    }
-    __syncthreads();
-    if (n < kTile) {
-      // partial tile: per-token rule on each row
-      for (int r = 0; r < n; ++r) {
-        const uint32_t x0 = xs[r * kChanRow + lane], x1 = xs[r * kChanRow + 64 + lane];
-        store_row(select_row(x0, x1, keep), x0, x1, bm + 2 * r, vals + r * keep);
-      }
-      continue;
-    }
-    // full tile: channel-wise selection, lane t = row t
-    uint64_t w0 = 0, w1 = 0;
-    for (int c = 0; c < kHeadDim; ++c) {
-      const uint32_t key = xs[lane * kChanRow + c] & 0x7FFFu;
-      uint32_t tau = 0;
-      for (int bit = 14; bit >= 0; --bit) {
-        const uint32_t cand = tau | (1u << bit);
-        const int cnt = __popcll(__ballot(key >= cand));
-        if (cnt >= kc) tau = cand;
-        if (cnt == kc) break;
-      }
-      const uint64_t gt = __ballot(key > tau), eq = __ballot(key == tau);
-      const int need = kc - __popcll(gt);
-      const bool kept = key > tau || (key == tau && (int)mbcnt64(eq, 0u) < need);
-      const uint64_t bitc = kept ? 1ull : 0ull;
-      if (c < 64) w0 |= bitc << c;
-      else w1 |= bitc << (c - 64);
-    }
-    *reinterpret_cast<uint4*>(bm + 2 * lane) =
-        make_uint4((uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32));
-    // pack the row's kept values (ascending channel) after the earlier rows'
-    const uint32_t pc = (uint32_t)(__popcll(w0) + __popcll(w1));
-    uint32_t pos = wave_excl_scan(pc);
-    const int most = (int)wave_uniform(wave_max_u32(pc));
-    uint64_t cur = w0;
-    uint32_t cbase = 0;
-    for (int i = 0; i < most; ++i) {
-      if (cur == 0ull && cbase == 0u) {
-        cur = w1;
-        cbase = 64u;
-      }
-      if (cur != 0ull) {
-        const uint32_t c = cbase + (uint32_t)__builtin_ctzll(cur);
-        cur &= cur - 1ull;
-        packed[pos++] = xs[lane * kChanRow + c];
-      }
-    }
-    __syncthreads();
-    for (int i = (int)lane; i < kTile * keep; i += kWave) vals[i] = packed[i];
-  }
+namespace {
+
+// The per-lane kernel over every 64-row tile of the (batch, head) units.
+hipError_t launch_lane(PruneArgs& a, int64_t units, int64_t tiles, bool channel, hipStream_t stream,
+                       const int32_t* seq_lens) {
+  constexpr int lds = kLaneWaves * kLaneTileBytes;
+  hipError_t e = channel ? ensure_lds_limit<&prune_lane_kernel<true>>(lds)
+                         : ensure_lds_limit<&prune_lane_kernel<false>>(lds);
+  if (e != hipSuccess) return e;
+  int cus = 0;
+  e = device_cu_count(&cus);
+  if (e != hipSuccess) return e;
+  const int64_t items = units * tiles;
+  if (items > INT32_MAX) return hipErrorInvalidValue;
+  a.tiles_per_unit = (int32_t)tiles;
+  a.items = (int32_t)items;
+  const int64_t want = (items + kLaneWaves - 1) / kLaneWaves;
+  const int64_t resident = (int64_t)cus * kLaneBlocksPerCu;
+  const dim3 grid((unsigned)(want < resident ? want : resident));
+  if (channel)
+    hipLaunchKernelGGL(prune_lane_kernel<true>, grid, dim3(kLaneBlock), lds, stream, a, seq_lens);
+  else
+    hipLaunchKernelGGL(prune_lane_kernel<false>, grid, dim3(kLaneBlock), lds, stream, a, seq_lens);
+  return hipGetLastError();
+}
+
+PruneArgs prune_args(const mustafar_kv_t& d, const KeepMap& map, const uint16_t* dense,
+                     int64_t t_stride, const int32_t* seq_lens, int64_t rows_per_unit, int64_t units) {
+  PruneArgs a;
+  a.dense = dense;
+  a.t_stride = t_stride;
+  a.seq_lens = seq_lens;
+  a.H = d.num_kv_heads;
+  a.cap = d.capacity;
+  a.rows_per_unit = (int32_t)rows_per_unit;
+  a.units = (int32_t)units;
+  a.bitmaps = d.bitmaps;
+  a.values = d.values;
+  a.tile_off = d.tile_offsets;
+  a.map = map;
+  a.tiles_per_unit = 0;
+  a.items = 0;
+  return a;
 }
 
 }  // namespace
@@ -441,22 +472,8 @@ hipError_t launch_prune_compress_channel(const mustafar_kv_t& d, const KeepMap& 
   const int64_t units = (int64_t)d.batch * d.num_kv_heads;
   const int64_t tiles = (rows_per_unit + kTile - 1) / kTile;
   if (units <= 0 || tiles <= 0) return hipSuccess;
-  const unsigned gy = (unsigned)(units < 65535 ? units : 65535);
-  PruneArgs a;
-  a.dense = dense;
-  a.t_stride = t_stride;
-  a.seq_lens = seq_lens;
-  a.H = d.num_kv_heads;
-  a.cap = d.capacity;
-  a.rows_per_unit = (int32_t)rows_per_unit;
-  a.units = (int32_t)units;
-  a.bitmaps = d.bitmaps;
-  a.values = d.values;
-  a.tile_off = d.tile_offsets;
-  a.map = map;
-  const int lds = (kTile * kChanRow + kTile * d.keep) * 2;
-  hipLaunchKernelGGL(prune_channel_kernel, dim3((unsigned)tiles, gy), dim3(kWave), lds, stream, a);
-  return hipGetLastError();
+  PruneArgs a = prune_args(d, map, dense, t_stride, seq_lens, rows_per_unit, units);
+  return launch_lane(a, units, tiles, true, stream, seq_lens);
 }
 
 hipError_t launch_prune_compress(const mustafar_kv_t& d, const KeepMap& map, const uint16_t* dense,
@@ -466,38 +483,11 @@ hipError_t launch_prune_compress(const mustafar_kv_t& d, const KeepMap& map, con
   const int64_t units = (int64_t)d.batch * d.num_kv_heads;
   const int64_t tiles = (rows_per_unit + kTile - 1) / kTile;
   if (units <= 0 || tiles <= 0) return hipSuccess;
+  PruneArgs a = prune_args(d, map, dense, t_stride, seq_lens, rows_per_unit, units);
+  if (!two_four) return launch_lane(a, units, tiles, false, stream, seq_lens);
   const unsigned gy = (unsigned)(units < 65535 ? units : 65535);
-  PruneArgs a;
-  a.dense = dense;
-  a.t_stride = t_stride;
-  a.seq_lens = seq_lens;
-  a.H = d.num_kv_heads;
-  a.cap = d.capacity;
-  a.rows_per_unit = (int32_t)rows_per_unit;
-  a.units = (int32_t)units;
-  a.bitmaps = d.bitmaps;
-  a.values = d.values;
-  a.tile_off = d.tile_offsets;
-  a.map = map;
-  if (two_four) {
-    hipLaunchKernelGGL(prune_compress_kernel<true>, dim3((unsigned)tiles, gy), dim3(kPruneBlock), 0,
-                       stream, a);
-  } else {
-    constexpr int lds = kLaneWaves * kLaneTileBytes;
-    hipError_t e = ensure_lds_limit<&prune_lane_kernel>(lds);
-    if (e != hipSuccess) return e;
-    int cus = 0;
-    e = device_cu_count(&cus);
-    if (e != hipSuccess) return e;
-    const int64_t items = units * tiles;
-    if (items > INT32_MAX) return hipErrorInvalidValue;
-    a.tiles_per_unit = (int32_t)tiles;
-    a.items = (int32_t)items;
-    const int64_t want = (items + kLaneWaves - 1) / kLaneWaves;
-    const int64_t resident = (int64_t)cus * kLaneBlocksPerCu;
-    hipLaunchKernelGGL(prune_lane_kernel, dim3((unsigned)(want < resident ? want : resident)),
-                       dim3(kLaneBlock), lds, stream, a, seq_lens);
-  }
+  hipLaunchKernelGGL(prune_compress_kernel<true>, dim3((unsigned)tiles, gy), dim3(kPruneBlock), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

@@ -9,33 +9,30 @@
 // scalar unit), so one wave selects 64 rows at once.  The row's dwords first
 // get bit 15 of both halves set (the sign is not part of the key), then:
 //
-//   1. the top 7 key bits (14..8) of four channels packed in the bytes of a
-//      dword, each byte with bit 7 set: subtracting a candidate c (0..127)
-//      from every byte leaves bit 7 set exactly where the byte's field is
-//      >= c, with no borrow between bytes, so the count of keys whose top bits
-//      are >= c is a popcount of the masked difference (three instructions per
-//      four keys).  An MSB-first bisection finds t1, the top bits of the
-//      keep-th largest key.
-//   2. the same on key bits 7..1 of the channels whose top bits equal t1;
-//      channels above t1 count as the largest field, channels below as the
-//      smallest, so the count is again that of all keys >= the candidate.  The
-//      fields come from one saturating 16-bit window per half: max(key - t1 *
-//      256, 0) capped at 255, shifted down one bit.  This gives key bits 14..1
-//      of the keep-th largest key.
-//   3. its bit 0 and the kept set from two 16-bit comparisons of all keys:
-//      E = {key >= odd candidate}; the count of E decides bit 0, and with the
-//      other comparison O ({key >= candidate + 1} when bit 0 is 1, {key >=
-//      candidate - 1} when it is 0) E and O are the sets {key >= tau} and
-//      {key > tau}.  A comparison leaves bit 15 of each half set where key >=
-//      the candidate; a byte permute turns those bits of two dwords into four
-//      0x00 / 0xFF bytes, eight such dwords merge into one word by bit-field
-//      inserts, and a fixed bit permutation puts every channel at its own bit.
+//   1. key bits 14..8 of four channels packed in the bytes of a dword (bit 7
+//      of every byte set).  The number of fields >= a candidate c comes from
+//      two byte sums of absolute differences: for one field v,
+//      |v - (c - 1)| - |v - c| is +1 when v >= c and -1 otherwise, so
+//      sad(c - 1) - sad(c) + 128 is twice the count (two v_sad_u8 per four
+//      keys).  An MSB-first bisection finds t1, bits 14..8 of the keep-th
+//      largest key.
+//   2. the same on key bits 7..0 of the channels whose bits 14..8 equal t1,
+//      with 255 for the channels above t1 and 0 for those below, so the count
+//      is again that of all keys >= the candidate.  The fields come from one
+//      saturating 16-bit window per half, min(max(key - t1 * 256, 0), 255),
+//      low bytes packed.  This gives tau, the keep-th largest key.
+//   3. the sets {key >= tau} and {key > tau}: (key | 0x8000) - c keeps bit 15
+//      set exactly where key >= c, with no borrow between the halves; a byte
+//      permute spreads those bits of two dwords into four 0x00 / 0xFF bytes,
+//      eight such dwords merge into one word by bit-field inserts, and a fixed
+//      bit permutation puts every channel at its own bit.
 //   4. the kept set: every key above tau, plus, of the keys equal to tau, the
 //      ones in the lowest channels until `keep` are kept.
 //
-// The functions compile for the host too (plain fallbacks of the byte permute
-// and the 16-bit saturating window), so the same code is checked on the CPU
-// against the oracle's definition.
+// The functions compile for the host too (plain fallbacks of the byte
+// permute, the byte sum of absolute differences and the 16-bit saturating
+// window), so the same code is checked on the CPU against the oracle's
+// definition.
 #pragma once
 
 #include <stdint.h>
@@ -72,18 +69,6 @@ MUSTAFAR_HD uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
 
 MUSTAFAR_HD uint32_t popc32(uint32_t v) { return (uint32_t)__builtin_popcount(v); }
 
-// popcount(v) + acc as one v_bcnt_u32_b32 (left to itself the compiler turns a
-// running count into a tree of separate popcounts and three-input adds).
-MUSTAFAR_HD uint32_t popc_add(uint32_t v, uint32_t acc) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  uint32_t r;
-  asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(acc));
-  return r;
-#else
-  return popc32(v) + acc;
-#endif
-}
-
 // sum over the four bytes of |a_b - c_b|, plus acc (v_sad_u8).
 MUSTAFAR_HD uint32_t sad_u8(uint32_t a, uint32_t c, uint32_t acc) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -103,13 +88,15 @@ MUSTAFAR_HD uint32_t sad_u8(uint32_t a, uint32_t c, uint32_t acc) {
 // differences plus 128 is 2 * #{v >= c}.  Two v_sad_u8 per four fields.
 MUSTAFAR_HD uint32_t sad_count2(const uint32_t (&f)[32], uint32_t c) {
   const uint32_t cm = c - 0x01010101u;
-  uint32_t lo = 128u, hi = 0u;
+  uint32_t lo0 = 128u, lo1 = 0u, hi0 = 0u, hi1 = 0u;  // four independent chains
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    lo = sad_u8(f[i], cm, lo);
-    hi = sad_u8(f[i], c, hi);
+  for (int i = 0; i < 32; i += 2) {
+    lo0 = sad_u8(f[i], cm, lo0);
+    hi0 = sad_u8(f[i], c, hi0);
+    lo1 = sad_u8(f[i + 1], cm, lo1);
+    hi1 = sad_u8(f[i + 1], c, hi1);
   }
-  return lo - hi;
+  return (lo0 + lo1) - (hi0 + hi1);
 }
 
 // Per 16-bit half: max(a - b, 0), capped at 255.
@@ -249,6 +236,118 @@ MUSTAFAR_HD void lane_select_row(uint32_t (&x)[64], uint32_t keep, uint32_t (&bm
   keep_lowest128(eq, keep > ngt ? keep - ngt : 0u);
 #pragma unroll
   for (int w = 0; w < 4; ++w) bm[w] = gt[w] | eq[w];
+}
+
+// The bit at position i moves to position rotl5(i, 1): bit i of the low half
+// to bit 2i, bit i of the high half to bit 2i + 1 (index bits (i4 i3 i2 i1
+// i0) -> (i3 i2 i1 i0 i4): a byte permute for index bits 4, 3, then delta
+// swaps for 3/2, 2/1 and 1/0).
+MUSTAFAR_HD uint32_t shuffle32(uint32_t w) {
+  w = byte_perm(w, w, 0x03010200u);
+  uint32_t t = (w ^ (w >> 4)) & 0x00F000F0u;
+  w ^= t ^ (t << 4);
+  t = (w ^ (w >> 2)) & 0x0C0C0C0Cu;
+  w ^= t ^ (t << 2);
+  t = (w ^ (w >> 1)) & 0x22222222u;
+  w ^= t ^ (t << 1);
+  return w;
+}
+
+// Twice the number of the 64 byte fields of f that are >= c (see
+// sad_count2).
+MUSTAFAR_HD uint32_t sad_count2_64(const uint32_t (&f)[16], uint32_t c) {
+  const uint32_t cm = c - 0x01010101u;
+  uint32_t lo0 = 64u, lo1 = 0u, hi0 = 0u, hi1 = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    lo0 = sad_u8(f[i], cm, lo0);
+    hi0 = sad_u8(f[i], c, hi0);
+    lo1 = sad_u8(f[i + 1], cm, lo1);
+    hi1 = sad_u8(f[i + 1], c, hi1);
+  }
+  return (lo0 + lo1) - (hi0 + hi1);
+}
+
+// Channel-wise selection of the two channels one lane holds over a 64-row
+// tile ([README] "Part II": the channel-wise direction of magnitude pruning).
+// y[r] = row r's fp16 bits of channel 2l (low half) and 2l + 1 (high half).
+// Each channel keeps its kc (0..64) rows of largest magnitude key, ties to
+// the earlier row: lo[w] / hi[w] bit j <=> row 32w + j kept for the low /
+// high channel.  The steps are those of lane_select_row, on 64 keys per
+// channel with the two channels side by side: byte fields of four rows of one
+// channel per dword (from two permutes of two dwords each), the 16-bit window
+// and the comparisons with a threshold per half.  y is overwritten.
+MUSTAFAR_HD void lane_select_columns(uint32_t (&y)[64], uint32_t kc, uint32_t (&lo)[2],
+                                     uint32_t (&hi)[2]) {
+#pragma unroll
+  for (int r = 0; r < 64; ++r) y[r] |= kHalfTop;
+  const uint32_t kc2 = 2u * kc;
+  uint32_t fl[16], fh[16];
+  // byte bl of the low half and bh of the high half of rows 4i .. 4i + 3
+  auto fields = [&](uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t sel, int i) {
+    const uint32_t pa = byte_perm(a1, a0, sel), pb = byte_perm(a3, a2, sel);
+    fl[i] = byte_perm(pb, pa, 0x05040100u);
+    fh[i] = byte_perm(pb, pa, 0x07060302u);
+  };
+  // 1. key bits 14..8 (bytes 1 and 3, bit 7 set)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) fields(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3], 0x07030501u, i);
+  uint32_t t1l = kByteTop, t1h = kByteTop;
+#pragma unroll
+  for (int b = 6; b >= 0; --b) {
+    const uint32_t cl = t1l | (0x01010101u << b), ch = t1h | (0x01010101u << b);
+    t1l = sad_count2_64(fl, cl) >= kc2 ? cl : t1l;
+    t1h = sad_count2_64(fh, ch) >= kc2 ? ch : t1h;
+  }
+  const uint32_t u1l = t1l & 0x7Fu, u1h = t1h & 0x7Fu;
+  // 2. key bits 7..0 within each channel's t1 bucket (bytes 0 and 2 of the window)
+  const uint32_t base = (((u1h << 8) | 0x8000u) << 16) | ((u1l << 8) | 0x8000u);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    fields(window_u16x2(y[4 * i], base), window_u16x2(y[4 * i + 1], base), window_u16x2(y[4 * i + 2], base),
+           window_u16x2(y[4 * i + 3], base), 0x06020400u, i);
+  uint32_t t2l = 0u, t2h = 0u;
+#pragma unroll
+  for (int b = 7; b >= 0; --b) {
+    const uint32_t cl = t2l | (0x01010101u << b), ch = t2h | (0x01010101u << b);
+    t2l = sad_count2_64(fl, cl) >= kc2 ? cl : t2l;
+    t2h = sad_count2_64(fh, ch) >= kc2 ? ch : t2h;
+  }
+  // 3. rows >= tau and > tau per channel: bit 15 / 31 of y - tau, sixteen
+  // rows per word (low half: the low channel), then 64-bit row masks
+  const uint32_t taur = (((u1h << 8) | (t2h & 0xFFu)) << 16) | ((u1l << 8) | (t2l & 0xFFu));
+  auto rows_at_least = [&](uint32_t cr, uint32_t (&ml)[2], uint32_t (&mh)[2]) {
+    uint32_t g[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t d[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        d[k] = byte_perm(y[16 * q + 2 * k + 1] - cr, y[16 * q + 2 * k] - cr, 0x0B0A0908u);
+      g[q] = shuffle32(merge_byte_masks(d));  // low half: rows of the low channel
+    }
+    ml[0] = byte_perm(g[1], g[0], 0x05040100u);
+    ml[1] = byte_perm(g[3], g[2], 0x05040100u);
+    mh[0] = byte_perm(g[1], g[0], 0x07060302u);
+    mh[1] = byte_perm(g[3], g[2], 0x07060302u);
+  };
+  uint32_t gel[2], geh[2], gtl[2], gth[2];
+  rows_at_least(taur, gel, geh);
+  rows_at_least(taur + 0x00010001u, gtl, gth);
+  // 4. rows > tau, then rows == tau from the earliest
+  auto finish = [&](const uint32_t (&ge)[2], const uint32_t (&gt)[2], uint32_t (&out)[2]) {
+    const uint32_t ngt = popc32(gt[0]) + popc32(gt[1]);
+    uint32_t n = kc > ngt ? kc - ngt : 0u;
+    uint32_t e0 = ge[0] & ~gt[0], e1 = ge[1] & ~gt[1];
+    const uint32_t c0 = popc32(e0);
+    e0 = lowest_set_bits(e0, n);
+    n = n > c0 ? n - c0 : 0u;
+    e1 = lowest_set_bits(e1, n);
+    out[0] = gt[0] | e0;
+    out[1] = gt[1] | e1;
+  };
+  finish(gel, gtl, lo);
+  finish(geh, gth, hi);
 }
 
 }  // namespace mustafar
