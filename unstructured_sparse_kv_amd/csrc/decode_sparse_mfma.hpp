@@ -165,7 +165,8 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
   const auto vtrs = make_rsrc(a.vtoff + (int64_t)unit * ntoff, (uint32_t)ntoff * 4u);
   // chunks of each row's prefetch: a constant, so that no branch separates
   // the loads (without an exact keep, the whole register budget: the extra
-  // bytes are the next rows' and hit the cache)
+  // bytes are the next rows' and hit the cache; a count taken from the keep
+  // at run time measured slower)
   constexpr int kch = NK > 0 ? row_chunks(NK) : KW / 4;
   constexpr int vch = kch;
   const bool k_odd = (kk & 1) != 0, v_odd = (vk & 1) != 0;
@@ -365,14 +366,24 @@ hipError_t launch_mfma_t(const SparseDecodeArgs& a, int batch, hipStream_t strea
   return hipGetLastError();
 }
 
-// Straight-line walks for the keeps of 70% and 50% sparsity at head_dim 128
-// (38 and 64) when every head keeps the same; bucketed walks for any other keep
-// and for per-head keeps.
+// Straight-line walks when every head keeps the same number of values and it
+// is that of one of the sparsities 50, 60, 65, 70, 75 or 80% at head_dim 128
+// (keep 64, 51, 45, 38, 32, 26); bucketed walks for any other keep and for
+// per-head keeps.
 template <int G>
 hipError_t launch_mfma_g(const SparseDecodeArgs& a, int batch, hipStream_t stream) {
   const bool uniform = !a.kmap.per_head && !a.vmap.per_head;
-  if (uniform && a.kk == a.vk && a.kk == 38) return launch_mfma_t<G, 40, 38>(a, batch, stream);
-  if (uniform && a.kk == a.vk && a.kk == 64) return launch_mfma_t<G, 64, 64>(a, batch, stream);
+  if (uniform && a.kk == a.vk) {
+    switch (a.kk) {
+      case 26: return launch_mfma_t<G, 32, 26>(a, batch, stream);
+      case 32: return launch_mfma_t<G, 32, 32>(a, batch, stream);
+      case 38: return launch_mfma_t<G, 40, 38>(a, batch, stream);
+      case 45: return launch_mfma_t<G, 48, 45>(a, batch, stream);
+      case 51: return launch_mfma_t<G, 64, 51>(a, batch, stream);
+      case 64: return launch_mfma_t<G, 64, 64>(a, batch, stream);
+      default: break;
+    }
+  }
   const int kmax = a.kk > a.vk ? a.kk : a.vk;
   if (kmax <= 32) return launch_mfma_t<G, 32, 0>(a, batch, stream);
   if (kmax <= 48) return launch_mfma_t<G, 48, 0>(a, batch, stream);

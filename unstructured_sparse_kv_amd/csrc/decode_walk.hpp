@@ -153,10 +153,9 @@ __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, uint32_t sta
     row[4 * j + 0] = c.x; row[4 * j + 1] = c.y; row[4 * j + 2] = c.z; row[4 * j + 3] = c.w;
   }
   if (odd_possible) {
-    const bool odd = start & 1u;
+    const uint32_t sh = (start & 1u) << 4;  // 16 for an odd start, 0 (no change) otherwise
 #pragma unroll
-    for (int j = 0; j < KW - 1; ++j)
-      row[j] = odd ? __builtin_amdgcn_alignbit(row[j + 1], row[j], 16u) : row[j];
+    for (int j = 0; j < KW - 1; ++j) row[j] = __builtin_amdgcn_alignbit(row[j + 1], row[j], sh);
   }
 }
 
