@@ -678,6 +678,7 @@ def main() -> int:
         kheads = [28, 32, 34, 38, 38, 42, 44, 48]
         vheads = kheads[::-1]
         seq_h = torch.full((B,), T0, dtype=torch.int32, device=dev)
+        sh0 = np.full(B, T0, np.int32)
         kch = usk.CompressedKV(B, Hkv, None, cap, dev, head_keep=kheads)
         vch = usk.CompressedKV(B, Hkv, None, cap, dev, head_keep=vheads)
         usk.prune_compress(kch, K0, seq_h)
@@ -685,11 +686,30 @@ def main() -> int:
         torch.cuda.synchronize()
         hk_s = median(timed(lambda: usk.decode_attn(q_last, kch, vch, seq_h, cap, scale, out, ws), 10,
                             before=lambda: usk.probe_stream_read(flush, sink)))
-        sh0 = np.full(B, T0, np.int32)
         hk_bytes = kch.used_bytes(sh0) + vch.used_bytes(sh0)
         log(f"per-head keep K {kheads} / V {vheads}: decode after a 1 GiB read {hk_s * 1e6:.1f} us "
             f"({hk_bytes / hk_s / 1e9:.0f} GB/s, {hk_bytes} bytes)")
         del kch, vch
+
+        # ---- uniform keeps of the 50..80% sparsities (keep 64, 51, 45, 38, 32, 26):
+        # layer 0's dense caches pruned at each, decode after a 1 GiB read; GB/s on
+        # each keep's own compressed bytes, and relative to keep 38's
+        keep_sweep = {}
+        for kp in (26, 32, 38, 45, 51, 64):
+            kck = usk.CompressedKV(B, Hkv, kp, cap, dev)
+            vck = usk.CompressedKV(B, Hkv, kp, cap, dev)
+            usk.prune_compress(kck, K0, seq_h)
+            usk.prune_compress(vck, V0, seq_h)
+            torch.cuda.synchronize()
+            t_k = median(timed(lambda: usk.decode_attn(q_last, kck, vck, seq_h, cap, scale, out, ws), 10,
+                               before=lambda: usk.probe_stream_read(flush, sink)))
+            nb_k = kck.used_bytes(sh0) + vck.used_bytes(sh0)
+            keep_sweep[kp] = (t_k, nb_k)
+            del kck, vck
+        gbs38 = keep_sweep[38][1] / keep_sweep[38][0] / 1e9
+        for kp, (t_k, nb_k) in keep_sweep.items():
+            log(f"uniform keep {kp}: decode after a 1 GiB read {t_k * 1e6:.1f} us "
+                f"({nb_k / t_k / 1e9:.0f} GB/s, {nb_k / t_k / 1e9 / gbs38:.3f} of keep 38's)")
 
         # dense attention over layer 0's unpruned caches: the reference the pruned
         # variants below are compared with
@@ -754,6 +774,11 @@ def main() -> int:
         del k24, v24, k64, v64
 
         return {
+            "keep_sweep_after_1gib_read": {
+                str(kp): {"us": round(t_k * 1e6, 2), "bytes": int(nb_k), "gbs": round(nb_k / t_k / 1e9, 1),
+                          "of_keep38_gbs": round(nb_k / t_k / 1e9 / gbs38, 3)}
+                for kp, (t_k, nb_k) in keep_sweep.items()},
+            "head_keep_of_keep38_gbs": round(hk_bytes / hk_s / 1e9 / gbs38, 3),
             "head_keep_k": kheads,
             "head_keep_v": vheads,
             "head_keep_decode_us_after_1gib_read": round(hk_s * 1e6, 2),
@@ -908,6 +933,8 @@ def main() -> int:
             "dense_us_b8_after_1gib_read": round(dense[8] * 1e6, 2),
             "dense_us_b6_after_1gib_read": round(dense[6] * 1e6, 2),
             "speedup_vs_dense_b8": round(dense[8] / cold_s, 3),
+            "pv_arithmetic": "both kernels: fp32 softmax, P.V with p rounded to fp16 and fp32 "
+                             "accumulation (sparse on the matrix cores, dense on the vector units)",
             "tokens_per_s_ratio_sparse_b8_vs_dense_b6": round((8 / cold_s) / (6 / dense[6]), 3),
             "pages_tokens_per_s_ratio_b8_vs_b6": 2.23,
         })

@@ -370,7 +370,9 @@ int mustafar_decode_attn_24(const uint16_t *q, int32_t num_q_heads, const mustaf
  * The same attention over dense, unpruned fp16 caches: the comparison
  * baseline (the pages compare against dense attention, [Summary] "Key results"
  * and "Experimental setup").  q.K^T runs on the matrix cores (MFMA), P.V and
- * the softmax on the vector units (fp32); two launches like mustafar_decode_attn.
+ * the softmax on the vector units: fp32 softmax, P.V with the probabilities
+ * rounded to fp16 and fp32 accumulation (the operand precisions of
+ * mustafar_decode_attn); two launches like mustafar_decode_attn.
  *
  *   k, v (device) uint16 [batch][num_kv_heads][t_stride][128] fp16 bits; rows
  *        t < min(seq_lens[b], t_stride) are attended.

@@ -11,6 +11,8 @@
 //           x 4 channel blocks = 16 MFMAs per tile.
 //   P.V     vector units: lane l owns channels 8*(l%16)..+7 of rows 4i + l/16,
 //           fp32 accumulators for every head; lane groups are summed at the end.
+//           The probabilities enter rounded to fp16 (their sum stays fp32), as
+//           in the sparse kernels, so that the two compare like for like.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "merge.hpp"
@@ -118,7 +120,8 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_dense_kernel(DenseDecodeA
       for (int i = 0; i < 4; ++i) {
         const float p = exp2f(sv[4 * mb + i] - mn);
         ps += p;
-        if ((int)l16 < G) p_lds[(16 * mb + 4 * grp + i) * G + l16] = p;
+        // P.V takes p rounded to fp16, the sparse kernels' operand precision
+        if ((int)l16 < G) p_lds[(16 * mb + 4 * grp + i) * G + l16] = (float)(_Float16)p;
       }
     lsum = lsum * alpha + ps;
     m = mn;
