@@ -173,6 +173,7 @@ void decode_24_kernel(SparseDecodeArgs a) {
   };
 
   for (int tile = tb; tile < te; ++tile) {
+    set_priority_by_tiles_left(te - tile, tpw);
     const int nvalid = min(kTile, T - tile * kTile);
     const bool valid = (int)lane < nvalid;
     const bool partial = nvalid < kTile;

@@ -147,6 +147,7 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
   }
 
   for (int tile = tb; tile < te; ++tile) {
+    set_priority_by_tiles_left(te - tile, tpw);
     const int nvalid = min(kTile, T - tile * kTile);
     const bool valid = (int)lane < nvalid;
     const bool partial = nvalid < kTile;

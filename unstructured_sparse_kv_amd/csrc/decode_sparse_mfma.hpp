@@ -326,8 +326,12 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
   // tail masks nor the patch.
   const bool has_last = tb < te && te == ntiles;
   const int te_plain = has_last ? te - 1 : te;
-  for (int tile = tb; tile < te_plain; ++tile) do_tile(tile, std::false_type{}, std::false_type{});
+  for (int tile = tb; tile < te_plain; ++tile) {
+    set_priority_by_tiles_left(te - tile, tpw);
+    do_tile(tile, std::false_type{}, std::false_type{});
+  }
   if (has_last) {
+    set_priority_by_tiles_left(1, tpw);
     if (owner)
       do_tile(te - 1, std::true_type{}, std::true_type{});
     else

@@ -75,6 +75,26 @@ __device__ __forceinline__ T wave_uniform(T x) {
   return __builtin_amdgcn_readfirstlane(x);
 }
 
+// Split kernels run two blocks per compute unit, so each SIMD holds one wave of
+// each.  The SIMD's issue arbiter prefers the older wave, so the block
+// dispatched first finishes its tiles well before the other, which then runs
+// its last tiles alone at one wave per SIMD (a sixth of the kernel at the
+// Llama-3 layer shape).  A wave's priority therefore falls as its share of
+// tiles runs out: 3 while more than half is left, then 2, 1 and 0 below a
+// half, a quarter and an eighth.  A wave that has fallen behind then wins
+// the arbitration, and the two finish together.  `left` and `share` are
+// uniform across the wave.
+__device__ __forceinline__ void set_priority_by_tiles_left(int left, int share) {
+  if (2 * left > share)
+    __builtin_amdgcn_s_setprio(3);
+  else if (4 * left > share)
+    __builtin_amdgcn_s_setprio(2);
+  else if (8 * left > share)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
