@@ -45,7 +45,6 @@ int scratch_of_current_device(void** out) {
   return MUSTAFAR_OK;
 }
 
-constexpr int kMaxSplits = 1024;
 constexpr int64_t kMaxCapacity = 1 << 24;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

@@ -230,16 +230,38 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
     vb = buf_load16(vbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
     load_row<KW>(vrs, t0 + lane * (uint32_t)vk, vch, !kEvenExact && (v_odd || (t0 & 1u)), vrow);
   };
-  if (tb < te) {
-    offsets(tb, kt0, vt0);
-    issue_k(tb, kt0);
-    issue_v(tb, vt0);
-  }
+  // The first tile's rows are requested at once, from where every cache the
+  // library writes puts them (each earlier row holds exactly its head's
+  // keep), instead of after the stored offsets arrive: a second dependent
+  // memory round trip at kernel start.  A stored offset that differs (checked
+  // once the buffer is clear) requests them again.  The requests are not
+  // conditional (a wave without tiles reads in-range bytes or gets zeros from
+  // the range check), so that waiting for the offsets does not also wait for
+  // the rows.
+  kt0 = (uint32_t)(tb * kTile) * (uint32_t)kk;
+  vt0 = (uint32_t)(tb * kTile) * (uint32_t)vk;
+  issue_k(tb, kt0);
+  issue_v(tb, vt0);
   const uint32_t tile_base = (uint32_t)(tile_lds - smem);
   // the buffer starts clean; afterwards the operand reads clear it
-  for (uint32_t o = 8u * lane; o < (uint32_t)kTileBytes; o += 8u * kWave)
-    *reinterpret_cast<uint2*>(tile_lds + o) = make_uint2(0u, 0u);
+  static_assert(kTileBytes % 16 == 0, "tile buffer cleared in 16-byte stores");
+  constexpr int kClearFull = kTileBytes / (16 * kWave) * (16 * kWave);
+#pragma unroll
+  for (int o = 0; o < kClearFull; o += 16 * kWave)
+    *reinterpret_cast<uint4*>(tile_lds + o + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+  if (kClearFull + 16 * (int)lane < kTileBytes)
+    *reinterpret_cast<uint4*>(tile_lds + kClearFull + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
   wave_lds_sync();
+  if (tb < te) {
+    uint32_t kts, vts;
+    offsets(tb, kts, vts);
+    if (kts != kt0 || vts != vt0) {
+      kt0 = kts;
+      vt0 = vts;
+      issue_k(tb, kt0);
+      issue_v(tb, vt0);
+    }
+  }
   // An MFMA operand (16 bytes) read and cleared.
   auto take16 = [&](const char* p) {
     uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<char*>(p));

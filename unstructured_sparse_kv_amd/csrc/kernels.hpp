@@ -15,6 +15,7 @@ namespace mustafar {
 constexpr int kDecodeWaves = 4;        // waves per decode block
 constexpr int kDecodeBlock = kDecodeWaves * 64;
 constexpr int kPartStride = 132;       // floats per (unit, split, q head) partial: m, l, acc[128], pad
+constexpr int kMaxSplits = 1024;       // sequence splits per (batch, kv head)
 
 // Survivors per row of each kv head of one compressed tensor, and where the
 // value region of (batch b, head h) starts: element cap * (b * sum + before(h)),

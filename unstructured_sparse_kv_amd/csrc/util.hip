@@ -27,55 +27,84 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 
 // Merge the split partials of one (batch, q head): block (b*Hq + hq).
 // M = max m_s, L = sum l_s 2^(m_s - M), out = sum acc_s 2^(m_s - M) / L
-// (0 for an empty sequence).  The 256 threads first take the maximum over the
-// splits together; then thread t sums channel t % 128 over the splits of
-// parity t / 128, with the loop unrolled so that several splits' loads are in
-// flight at once (the partials were just written and sit in the L2), and the
-// two halves are added in LDS.
+// (0 for an empty sequence).  Thread t sums channel t % 128 over the splits of
+// parity t / 128 (a wave-uniform value), and the two halves are added in LDS.
+// The partials were written by the split kernel just before, so every load is
+// a memory round trip: m and l of every split, then the accumulators of the
+// first 2 * NV splits (they do not depend on M), are all requested at the
+// start, and the factors 2^(m_s - M) go through LDS, so the merge waits for
+// one round trip instead of one per batch of splits.  NV is the smallest of
+// 4, 8, 16, 32 that covers the splits (more than 64 splits: the rest in a loop).
 constexpr int kReduceThreads = 2 * kHeadDim;
 
+template <int NV>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(
     const float* __restrict__ part, int hq_total, int g_size, int splits, uint16_t* __restrict__ out,
     int32_t* seq_lens, uint32_t* status, int32_t cap, int advance) {
-  __shared__ float red[kReduceThreads / kWave];
+  __shared__ float fs[kMaxSplits];  // 2^(m_s - M), 0 for an empty split
+  __shared__ float red_m[kReduceThreads / kWave];
+  __shared__ float red_l[kReduceThreads / kWave];
   __shared__ float half_a[kHeadDim];
-  __shared__ float half_l;
   const int bq = blockIdx.x;
   const int b = bq / hq_total, hq = bq % hq_total;
   const int hkv = hq_total / g_size;
   const int h = hq / g_size, g = hq % g_size;
   const int unit = b * hkv + h;
-  const int t = threadIdx.x, c = t % kHeadDim, par = t / kHeadDim;
+  const int t = threadIdx.x, c = t % kHeadDim, par = wave_uniform(t / kHeadDim);
   const float ninf = -__builtin_inff();
   const float* pu = part + ((int64_t)unit * splits * g_size + g) * kPartStride;
   const int64_t sstride = (int64_t)g_size * kPartStride;
 
-  float mx = ninf;
-  for (int s = t; s < splits; s += kReduceThreads) mx = fmaxf(mx, pu[s * sstride]);
-  mx = wave_max(mx);
-  if (lane_id() == 0) red[t / kWave] = mx;
-  __syncthreads();
-  float M = red[0];
+  // split t (splits <= kReduceThreads needs no other); clamped indices, so
+  // that no load is conditional and waiting for one does not wait for later ones
+  const float2 ml = *reinterpret_cast<const float2*>(pu + min(t, splits - 1) * sstride);
+  const float m0 = t < splits ? ml.x : ninf, l0 = t < splits ? ml.y : 0.f;
+  float v[NV];
 #pragma unroll
-  for (int w = 1; w < kReduceThreads / kWave; ++w) M = fmaxf(M, red[w]);
+  for (int j = 0; j < NV; ++j) {
+    const int sc = min(par + 2 * j, splits - 1);
+    v[j] = pu[sc * sstride + 2 + c];
+  }
+  float mx = m0;
+  for (int s = t + kReduceThreads; s < splits; s += kReduceThreads) mx = fmaxf(mx, pu[s * sstride]);
+  mx = wave_max(mx);
+  if (lane_id() == 0) red_m[t / kWave] = mx;
+  __syncthreads();
+  float M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < kReduceThreads / kWave; ++w) M = fmaxf(M, red_m[w]);
 
-  float A = 0.f, L = 0.f;
-#pragma unroll 8
-  for (int s = par; s < splits; s += 2) {
-    const float* ps = pu + s * sstride;
-    const float ms = ps[0];
+  float lp = 0.f;
+  if (t < splits) {
+    const float f = (m0 == ninf) ? 0.f : exp2f(m0 - M);
+    fs[t] = f;
+    lp = l0 * f;
+  }
+  for (int s = t + kReduceThreads; s < splits; s += kReduceThreads) {
+    const float ms = pu[s * sstride];
     const float f = (ms == ninf) ? 0.f : exp2f(ms - M);
-    A += ps[2 + c] * f;
-    L += ps[1] * f;
+    fs[s] = f;
+    lp += pu[s * sstride + 1] * f;
   }
-  if (par == 1) {
-    half_a[c] = A;
-    if (c == 0) half_l = L;
+  lp = wave_sum(lp);
+  if (lane_id() == 0) red_l[t / kWave] = lp;
+  __syncthreads();
+  float L = red_l[0];
+#pragma unroll
+  for (int w = 1; w < kReduceThreads / kWave; ++w) L += red_l[w];
+
+  float A = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int s = par + 2 * j;
+    if (s < splits) A += v[j] * fs[s];
   }
+#pragma unroll 8
+  for (int s = par + 2 * NV; s < splits; s += 2) A += pu[s * sstride + 2 + c] * fs[s];
+  if (par == 1) half_a[c] = A;
   __syncthreads();
   if (par == 0) {
     A += half_a[c];
-    L += half_l;
     out[(int64_t)bq * kHeadDim + c] = float_to_half_bits(L > 0.f ? A / L : 0.f);
   }
   // a fused decode step: the split kernel stored row seq_lens[b] (all its
@@ -95,8 +124,12 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(
 hipError_t launch_decode_reduce(const float* part, int batch, int hq, int hkv, int splits,
                                 uint16_t* out, hipStream_t stream, int32_t* seq_lens,
                                 uint32_t* status, int32_t cap, bool advance) {
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3(batch * hq), dim3(kReduceThreads), 0, stream, part, hq,
-                     hq / hkv, splits, out, seq_lens, status, cap, advance ? 1 : 0);
+  auto kernel = splits <= 8    ? decode_reduce_kernel<4>
+                : splits <= 16 ? decode_reduce_kernel<8>
+                : splits <= 32 ? decode_reduce_kernel<16>
+                               : decode_reduce_kernel<32>;
+  hipLaunchKernelGGL(kernel, dim3(batch * hq), dim3(kReduceThreads), 0, stream, part, hq, hq / hkv,
+                     splits, out, seq_lens, status, cap, advance ? 1 : 0);
   return hipGetLastError();
 }
 
