@@ -527,16 +527,8 @@ def main() -> int:
         usk.prune_compress(kc, K, seq_d)
         usk.prune_compress(vc, V, seq_d)
         torch.cuda.synchronize()
-        if layer == 0:  # prefill prune + compress timing (events)
-            for _ in range(3):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                usk.prune_compress(kc, K, seq_d)
-                usk.prune_compress(vc, V, seq_d)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                pre.append(e0.elapsed_time(e1) * 1e-3)
-            K0, V0 = K, V
+        if layer == 0:
+            K0, V0 = K, V  # kept for the prefill timing and the dense comparison
         else:
             del K, V
         kcs.append(kc)
@@ -547,9 +539,6 @@ def main() -> int:
     seq_host = np.full(B, T0, np.int32)
     comp_bytes0 = kcs[0].used_bytes(seq_host) + vcs[0].used_bytes(seq_host)
     dense_bytes0 = 2 * B * Hkv * T0 * d * 2
-    prefill_s = median(pre)
-    log(f"prefill prune+compress K and V: {prefill_s * 1e6:.1f} us "
-        f"({(dense_bytes0 + comp_bytes0) / prefill_s / 1e9:.0f} GB/s moved)")
 
     ws = usk.make_workspace(B, Hq, Hkv, cap)
     out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
@@ -577,6 +566,25 @@ def main() -> int:
             ramp_calls += 1
         torch.cuda.synchronize()
     log(f"clock ramp: {ramp_calls} read-only decode calls in {time.perf_counter() - t_r:.2f} s")
+
+    # prefill prune + compress of layer 0's K and V, timed at the same clocks
+    # (events around each pair of calls; every call rewrites layer 0's caches
+    # with the same bits: same dense input, same lengths)
+    for _ in range(2):
+        usk.prune_compress(kcs[0], K0, seqs[0])
+        usk.prune_compress(vcs[0], V0, seqs[0])
+    torch.cuda.synchronize()
+    for _ in range(9):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        usk.prune_compress(kcs[0], K0, seqs[0])
+        usk.prune_compress(vcs[0], V0, seqs[0])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pre.append(e0.elapsed_time(e1) * 1e-3)
+    prefill_s = median(pre)
+    log(f"prefill prune+compress K and V: {prefill_s * 1e6:.1f} us "
+        f"({(dense_bytes0 + comp_bytes0) / prefill_s / 1e9:.0f} GB/s moved)")
 
     for i in range(args.warmup):
         layer = i % NL
