@@ -149,8 +149,12 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
 
   const int total_waves = a.splits * kDecodeWaves;
   const int wid = s * kDecodeWaves + wave;
-  const int tpw = (ntiles + total_waves - 1) / total_waves;
-  const int tb = min(wid * tpw, ntiles), te = min(tb + tpw, ntiles);
+  // tiles split as evenly as their count allows: wave w takes [w n / W, (w + 1) n / W),
+  // so no wave has more than one tile above the average (a split by the rounded-up
+  // average gave 30 of 32 waves 17 tiles of a 513-tile unit, two waves 3 and 0)
+  const int tb = (int)((int64_t)wid * ntiles / total_waves);
+  const int te = (int)((int64_t)(wid + 1) * ntiles / total_waves);
+  const int tpw = te - tb;  // this wave's share
 
   constexpr uint32_t kKMapAt = offsetof(SparseDecodeArgs, kmap);
   constexpr uint32_t kVMapAt = offsetof(SparseDecodeArgs, vmap);
