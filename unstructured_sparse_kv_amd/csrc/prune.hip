@@ -242,6 +242,7 @@ __global__ __launch_bounds__(kLaneBlock) void prune_lane_kernel(PruneArgs a,
   char* const tl = smem + wave * kLaneTileBytes;  // this wave's LDS tile
   int item = (int)blockIdx.x * kLaneWaves + wave;
   if (item >= a.items) return;
+  const int share = (a.items - 1 - item) / nwaves + 1;  // this wave's tiles
   LaneTile cur = lane_tile(a, seq_lens, item);
   uint4 r[16];
   lane_fetch(a, cur, true, lane, r);
@@ -249,6 +250,7 @@ __global__ __launch_bounds__(kLaneBlock) void prune_lane_kernel(PruneArgs a,
     // r: the rows of tile `item`
     const int next = item + nwaves;
     const bool more = next < a.items;
+    set_priority_by_tiles_left((a.items - 1 - item) / nwaves + 1, share);
     uint32_t* toff = a.tile_off + (int64_t)cur.unit * ntoff;
     if (cur.tile == 0 && lane == 0 && cur.T == 0) toff[0] = 0;
     const int keep = keep_of(a.map, kMapAt, cur.h);
