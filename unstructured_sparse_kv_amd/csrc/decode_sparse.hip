@@ -136,13 +136,14 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
   uint4 kb, vb;
   uint32_t krow[KW], vrow[KW];
   uint32_t kt0 = 0, vt0 = 0, kt0n = 0, vt0n = 0;
+  // (rows starting at an odd value are realigned when their tile is walked)
   auto issue_k = [&](int tile, uint32_t t0) {
     kb = buf_load16(kbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
-    load_row<KW>(krs, t0 + lane * (uint32_t)kk, kch, !kEvenExact && (k_odd || (t0 & 1u)), krow);
+    load_row_raw<KW>(krs, t0 + lane * (uint32_t)kk, kch, krow);
   };
   auto issue_v = [&](int tile, uint32_t t0) {
     vb = buf_load16(vbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
-    load_row<KW>(vrs, t0 + lane * (uint32_t)vk, vch, !kEvenExact && (v_odd || (t0 & 1u)), vrow);
+    load_row_raw<KW>(vrs, t0 + lane * (uint32_t)vk, vch, vrow);
   };
   if (tb < te) {
     offsets(tb, kt0, vt0);
@@ -170,6 +171,7 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
       for (int g = 0; g < G; ++g) sc[g] = fmaf(v, half_bits_to_float(qh[g]), sc[g]);
     };
     // lanes past the end read q entries like the others; their scores are masked
+    if (!kEvenExact && (k_odd || (kt0 & 1u))) realign_row<KW>(kt0 + lane * (uint32_t)kk, krow);
     decode_side<NMAX, NK, true, C::kQMul>(krs, kt0, kk, valid, partial, !kEvenExact || !(kt0 & 1u),
                                           kb, krow, 0u, 0u, score);
     issue_k(nxt, kt0n);
@@ -205,6 +207,7 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_sparse_kernel(SparseDecod
       *reinterpret_cast<uint16_t*>(smem + addr) = (uint16_t)vbits;
     };
     const uint32_t col = (uint32_t)(vt_lds - smem) + 2u * lane;
+    if (!kEvenExact && (v_odd || (vt0 & 1u))) realign_row<KW>(vt0 + lane * (uint32_t)vk, vrow);
     decode_side<NMAX, NK, false, kTRowBytes>(vrs, vt0, vk, valid, partial,
                                              !kEvenExact || !(vt0 & 1u), vb, vrow, col, 0u, scatter);
     issue_v(nxt, vt0n);

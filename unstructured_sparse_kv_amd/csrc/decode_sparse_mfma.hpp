@@ -226,13 +226,14 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
   uint4 kb, vb;
   uint32_t krow[KW], vrow[KW];
   uint32_t kt0 = 0, vt0 = 0, kt0n = 0, vt0n = 0;
+  // (rows starting at an odd value are realigned when their tile is walked)
   auto issue_k = [&](int tile, uint32_t t0) {
     kb = buf_load16(kbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
-    load_row<KW>(krs, t0 + lane * (uint32_t)kk, kch, !kEvenExact && (k_odd || (t0 & 1u)), krow);
+    load_row_raw<KW>(krs, t0 + lane * (uint32_t)kk, kch, krow);
   };
   auto issue_v = [&](int tile, uint32_t t0) {
     vb = buf_load16(vbrs, ((uint32_t)(tile * kTile) + lane) * 16u);
-    load_row<KW>(vrs, t0 + lane * (uint32_t)vk, vch, !kEvenExact && (v_odd || (t0 & 1u)), vrow);
+    load_row_raw<KW>(vrs, t0 + lane * (uint32_t)vk, vch, vrow);
   };
   // The first tile's rows are requested at once, from where every cache the
   // library writes puts them (each earlier row holds exactly its head's
@@ -290,6 +291,7 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
 
     // ---- key tile K[t][c]
     wave_lds_sync();  // the previous tile's reads (and clears) of the buffer are done
+    if (!kEvenExact && (k_odd || (kt0 & 1u))) realign_row<KW>(kt0 + lane * (uint32_t)kk, krow);
     if constexpr (PATCH) take_new(new_lds, kb, krow);
     decode_side<NMAX, NK, false, 2u>(krs, kt0, kk, valid, partial, !kEvenExact || !(kt0 & 1u), kb,
                                      krow, tile_base + lane * kKRow, 0u, scatter,
@@ -318,6 +320,7 @@ void decode_sparse_mfma_kernel(SparseDecodeArgs a) {
     // the score operand reads (which cleared the buffer); only the compiler
     // must keep the order
     wave_lds_sync();
+    if (!kEvenExact && (v_odd || (vt0 & 1u))) realign_row<KW>(vt0 + lane * (uint32_t)vk, vrow);
     if constexpr (PATCH) take_new(new_lds + C::kNewSide, vb, vrow);
     decode_side<NMAX, NK, false, kVRow>(
         vrs, vt0, vk, valid, partial, !kEvenExact || !(vt0 & 1u), vb, vrow, tile_base + 2u * lane,
