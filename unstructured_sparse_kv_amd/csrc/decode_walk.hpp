@@ -122,20 +122,29 @@ struct GeneralWalk {
     cur = cw[0]; b0 = cb[0]; n1 = cw[1]; b1 = cb[1]; n2 = cw[2]; b2 = cb[2]; n3 = cw[3]; b3 = cb[3];
   }
   // The next `iters` set bits (uniform across the wave), paired with values
-  // 0 .. iters-1 of `row`.
+  // 0 .. iters-1 of `row`.  Values past a lane's own count must be zero in
+  // `row` (the callers mask them): the walk then runs in chunks of 8 steps with
+  // no test per step, since a step past every lane's last set bit stores that
+  // zero at the dump slot.  (Per-step tests cost 12-16% on channel-wise caches,
+  // where every tile takes this walk.)
   template <int NMAX, int KW, class F>
   __device__ __forceinline__ void run(const uint32_t (&row)[KW], int iters, F&& f) {
+    auto step = [&](int i) {
+      f(cur ? b0 + (uint32_t)__builtin_ctz(cur) * MUL : dump, value_at(row, i));
+      cur &= cur - 1u;
+      const bool z = (cur == 0u);
+      cur = z ? n1 : cur; b0 = z ? b1 : b0;
+      n1 = z ? n2 : n1; b1 = z ? b2 : b1;
+      n2 = z ? n3 : n2; b2 = z ? b3 : b2;
+      n3 = z ? 0u : n3; b3 = z ? dump : b3;
+    };
+    constexpr int kChunk = 8;
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) {
-      if (i < iters) {
-        f(cur ? b0 + (uint32_t)__builtin_ctz(cur) * MUL : dump, value_at(row, i));
-        cur &= cur - 1u;
-        const bool z = (cur == 0u);
-        cur = z ? n1 : cur; b0 = z ? b1 : b0;
-        n1 = z ? n2 : n1; b1 = z ? b2 : b1;
-        n2 = z ? n3 : n2; b2 = z ? b3 : b2;
-        n3 = z ? 0u : n3; b3 = z ? dump : b3;
-      }
+    for (int i0 = 0; i0 < NMAX; i0 += kChunk) {
+      if (i0 >= iters) break;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j)
+        if (i0 + j < NMAX) step(i0 + j);
     }
   }
 };
