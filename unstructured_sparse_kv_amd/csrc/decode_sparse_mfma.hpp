@@ -12,13 +12,13 @@
 // Per tile, lane t of a wave owns row t of both caches (bitmaps and kept
 // entries in registers, loaded one tile ahead):
 //   key tile    walk the key bitmap and write each kept entry into a zeroed
-//               row-major fp16 tile K[t][c] in LDS (row stride 272 B).
+//               row-major fp16 tile K[t][c] in LDS (row stride 264 B).
 //   scores      v_mfma_f32_16x16x32_f16: A = 16 tile rows x 32 channels read
 //               from LDS, B = the G query heads as columns (registers), 4 row
 //               blocks x 4 channel blocks; lane l ends with head l%16 of rows
 //               16*mb + 4*(l/16) + i.
 //   value tile  walk the value bitmap into a zeroed channel-major tile
-//               V[c][t] in the same LDS buffer (row stride 144 B), while the
+//               V[c][t] in the same LDS buffer (row stride 136 B), while the
 //               score MFMAs run.
 //   softmax     tile_softmax.hpp: per head, online; with G <= 4 the scores
 //               are first compacted onto the lanes of the padding heads; the
@@ -32,8 +32,12 @@
 // and leaves zeros: the operand reads of a tile cover every byte its walk can
 // write, so the buffer is clean for the next tile without a clearing pass.
 // Lanes past the end of the sequence therefore write zeros (into their own row
-// or column), never data outside the operand area.  The strides keep the
-// operand reads free of bank conflicts.
+// or column), never data outside the operand area.  The strides are the ones
+// at which a tile side's scatter and read-and-clear together cost the LDS
+// least (measured: 264 B against 272 B key rows, 475 against 552 cycles per
+// compute unit and wave-tile side; 136 B against 144 B value rows, 469 against
+// 531): at the 16-byte-aligned strides the 8-byte exchanges meet bank conflicts
+// that these 8-byte-aligned ones avoid.
 #pragma once
 
 #include "decode_walk.hpp"
@@ -51,10 +55,12 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kKRow = 272;  // key tile row: 128 fp16 + 16 B (general-walk dump slot, bank spread)
-constexpr uint32_t kVRow = 144;  // value tile channel row: 64 fp16 + 16 B
-// value tile + the general walk's dump row (channel 128); the key tile (64 x 272) fits too
-constexpr int kTileBytes = 129 * 144;
+constexpr uint32_t kKRow = 264;  // key tile row: 128 fp16 + 8 B (the general walk's dump slot)
+constexpr uint32_t kVRow = 136;  // value tile channel row: 64 fp16 + 8 B
+// value tile + the general walk's dump row (channel 128), rounded up to 16 B;
+// the key tile (64 x 264) fits too
+constexpr int kTileBytes = (129 * kVRow + 15) / 16 * 16;
+static_assert(64 * kKRow <= kTileBytes, "the key tile shares the value tile's buffer");
 
 
 template <int G, int KW>
