@@ -276,12 +276,13 @@ def bench_llama2_layer(args) -> int:
     step_s = median(ts)
     nbytes = kc.used_bytes(np.full(B, L - 1, np.int32)) + vc.used_bytes(np.full(B, L - 1, np.int32))
     achieved = nbytes / step_s / 1e9
-    # read-only decode at the final length, after the same read, and the dense kernel
-    dec_s = median(_timed(stream, lambda: usk.decode_attn(steps_in[-1][2], kc, vc, seq_d, cap, scale,
+    # read-only decode and the dense kernel over the same T0 rows, after the same read (the
+    # steps' final length, T0 + 55 rows, is 65 tiles: one wave of the 64 then walks two)
+    seq_t0 = torch.full((B,), T0, dtype=torch.int32, device=dev)
+    dec_s = median(_timed(stream, lambda: usk.decode_attn(steps_in[-1][2], kc, vc, seq_t0, T0, scale,
                                                           out, ws), 20, before))
     wsd = usk.make_workspace(B, Hq, Hkv, T0)
     outd = torch.empty_like(out)
-    seq_t0 = torch.full((B,), T0, dtype=torch.int32, device=dev)
     dense_s = median(_timed(stream, lambda: usk.dense_decode_attn(steps_in[-1][2], K, V, seq_t0, T0, scale,
                                                                   outd, wsd), 20, before))
     comp_t0 = kc.used_bytes(np.full(B, T0, np.int32)) + vc.used_bytes(np.full(B, T0, np.int32))
@@ -325,6 +326,7 @@ def bench_llama2_layer(args) -> int:
                          "sample": "the whole workload: prefill prune + compress of K and V and one decode "
                                    f"step over all {B * Hq} (batch, q head) pairs"},
         "extra": {"decode_only_us": round(dec_s * 1e6, 2), "dense_us": round(dense_s * 1e6, 2),
+                  "decode_only_and_dense_seq_len": T0,
                   "speedup_vs_dense": round(dense_s / dec_s, 3),
                   "prefill_compress_us": round(median(pre) * 1e6, 2),
                   "compressed_kv_bytes": int(comp_t0), "dense_kv_bytes": int(dense_bytes),
